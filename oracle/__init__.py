@@ -1,0 +1,117 @@
+"""CPU oracle for the attention forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library never links,
+loads or calls it, and it shares no code with the HIP path.
+
+The arithmetic lives in ``fa2_oracle.c`` (plain C, IEEE double, one score
+row at a time, no -ffast-math).  This module only builds that file with gcc
+and marshals arrays into it through ctypes.
+
+Every function of the oracle is pinned by ``tests/test_oracle.py`` to closed
+forms, invariants, a library special case and a 50-digit brute force; none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fa2_oracle.c")
+_LIB = os.path.join(_HERE, "libfa2_oracle.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile fa2_oracle.c into oracle/libfa2_oracle.so with gcc."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _bind(lib):
+    lib.fa2_oracle_fwd.restype = ctypes.c_int
+    lib.fa2_oracle_fwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+    ]
+    lib.fa2_oracle_max_threads.restype = ctypes.c_int
+    lib.fa2_oracle_max_threads.argtypes = []
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().fa2_oracle_max_threads())
+
+
+def _as_f32(x) -> np.ndarray:
+    """Exact float32 carrier of the input values (fp32 as is, bf16 widened)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu")
+            if x.dtype not in (torch.float32, torch.bfloat16):
+                raise TypeError(f"oracle inputs must be float32 or bfloat16, got {x.dtype}")
+            x = x.to(torch.float32).contiguous().numpy()
+    except ImportError:  # pragma: no cover - torch is always present here
+        pass
+    a = np.asarray(x)
+    if a.dtype != np.float32:
+        raise TypeError(f"oracle inputs must carry float32 values, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def attention(q, k, v, scale: float, causal: bool, rows: Optional[np.ndarray] = None,
+              threads: int = 0, _lib_override=None):
+    """Reference attention forward.
+
+    q: [B,H,M,D], k/v: [B,H,N,D] (torch tensors or float32 numpy arrays).
+    rows: optional int64 array of query rows (same for every head); when
+    given, outputs cover only those rows.
+    Returns (o, lse) as float64 numpy arrays: o [B,H,R,D], lse [B,H,R].
+    """
+    qa, ka, va = _as_f32(q), _as_f32(k), _as_f32(v)
+    if qa.ndim != 4 or ka.ndim != 4 or va.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B,H,seq,D]")
+    B, H, M, D = qa.shape
+    N = ka.shape[2]
+    if ka.shape != (B, H, N, D) or va.shape != (B, H, N, D):
+        raise ValueError(f"shape mismatch q{qa.shape} k{ka.shape} v{va.shape}")
+    if rows is not None:
+        rows_a = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        R = rows_a.shape[0]
+        rows_p = rows_a.ctypes.data
+    else:
+        rows_a = None
+        R = M
+        rows_p = None
+    o = np.empty((B, H, R, D), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
+    lib = _load() if _lib_override is None else _lib_override
+    rc = lib.fa2_oracle_fwd(qa.ctypes.data, ka.ctypes.data, va.ctypes.data,
+                                o.ctypes.data, lse.ctypes.data, B, H, M, N, D,
+                                float(scale), int(bool(causal)), rows_p, R, int(threads))
+    if rc != 0:
+        raise ValueError(f"fa2_oracle_fwd failed with status {rc}")
+    del rows_a
+    return o, lse

@@ -1,0 +1,139 @@
+"""Seeded synthetic attention workloads.
+
+This module only draws random inputs and names the shapes; it holds none of
+the attention arithmetic.  Both the HIP path's tests/bench and the CPU oracle
+take their inputs from here, so the two sides always see identical values.
+
+Recipe (the pages measure on seeded ``torch.randn`` tensors only, never on a
+dataset -- "FlashAttention-2 from PyTorch to Triton", test and bench harness
+listings; "Writing FlashAttention 2 in Triton", numerics verification
+harness):
+
+* a CPU ``torch.Generator`` seeded with ``seed`` draws Q, then K, then V as
+  float32 standard normals of the full [B,H,M,D] / [B,H,N,D] shapes;
+* Q and K are multiplied by ``qk_sigma`` and V by ``v_sigma`` (both 1 unless
+  a workload stresses the max subtraction);
+* for bf16 workloads the float32 draws are rounded to bfloat16 with
+  round-to-nearest-even (``Tensor.to``).  The oracle then consumes exactly
+  those rounded values.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "torch_dtype"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    M: int
+    N: int
+    D: int
+    dtype: str          # "f32" or "bf16"
+    causal: bool
+    qk_sigma: float = 1.0
+    v_sigma: float = 1.0
+    seed: int = 0
+    # number of query rows per head checked against the oracle; None = all
+    sample_rows: Optional[int] = None
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def flops(self) -> float:
+        """Counted work 4*B*H*M*N*D, halved when causal.
+
+        This is the accounting of the bench harness in "FlashAttention-2 from
+        PyTorch to Triton" (two matmuls of M*N*D multiply-adds, halved for
+        causal), generalised to M != N.
+        """
+        f = 4.0 * self.B * self.H * self.M * self.N * self.D
+        return f / 2 if self.causal else f
+
+    @property
+    def elt_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def compulsory_bytes(self) -> int:
+        """Read Q, K, V once and write O and the fp32 logsumexp once."""
+        bh = self.B * self.H
+        return bh * (2 * self.M * self.D + 2 * self.N * self.D) * self.elt_bytes + 4 * bh * self.M
+
+    def describe(self) -> str:
+        return (f"{self.name}: B={self.B},H={self.H},M={self.M},N={self.N},D={self.D},"
+                f"{self.dtype},{'causal' if self.causal else 'non-causal'}")
+
+
+WORKLOADS = {
+    # tiny fp32 self-attention, the case the oracle runs in full in milliseconds
+    "tiny_f32": Workload("tiny_f32", 1, 1, 128, 128, 64, "f32", False, seed=1),
+    # the fp32 shape the CUDA project page benchmarks (B=4,H=12,M=N=2048,D=64)
+    "mha_f32_2k": Workload("mha_f32_2k", 4, 12, 2048, 2048, 64, "f32", False, seed=2),
+    # causal bf16, head dim 128
+    "causal_bf16_4k": Workload("causal_bf16_4k", 4, 16, 4096, 4096, 128, "bf16", True, seed=3),
+    # long-context causal bf16; the oracle checks a seeded sample of 512 rows per head
+    "causal_bf16_16k": Workload("causal_bf16_16k", 1, 32, 16384, 16384, 128, "bf16", True,
+                                seed=4, sample_rows=512),
+    # ragged cross-attention; Q,K ~ N(0, 4^2) so scores reach ~90 (past fp32 exp overflow)
+    "ragged_bf16_cross": Workload("ragged_bf16_cross", 8, 8, 1000, 3000, 64, "bf16", False,
+                                  qk_sigma=4.0, seed=5),
+}
+
+ORDER = ["tiny_f32", "mha_f32_2k", "causal_bf16_4k", "causal_bf16_16k", "ragged_bf16_cross"]
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def torch_dtype(dtype: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+
+
+def make_inputs(B: int, H: int, M: int, N: int, D: int, dtype: str = "f32", seed: int = 0,
+                qk_sigma: float = 1.0, v_sigma: float = 1.0):
+    """Draw (q, k, v) on the CPU, contiguous, in the I/O dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, H, M, D), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H, N, D), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, N, D), generator=g, dtype=torch.float32)
+    if qk_sigma != 1.0:
+        q.mul_(qk_sigma)
+        k.mul_(qk_sigma)
+    if v_sigma != 1.0:
+        v.mul_(v_sigma)
+    td = torch_dtype(dtype)
+    if td != torch.float32:
+        q, k, v = q.to(td), k.to(td), v.to(td)
+    return q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def workload_inputs(w: Workload):
+    return make_inputs(w.B, w.H, w.M, w.N, w.D, w.dtype, w.seed, w.qk_sigma, w.v_sigma)
+
+
+def sample_rows(w: Workload, seed_offset: int = 1000):
+    """Seeded per-workload sample of query rows (same rows for every head).
+
+    Rows 0 and M-1 are always included; the rest are drawn uniformly without
+    replacement.  Returns a sorted int64 tensor, or None when every row is
+    checked.
+    """
+    if w.sample_rows is None or w.sample_rows >= w.M:
+        return None
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + seed_offset)
+    inner = torch.randperm(w.M - 2, generator=g)[: w.sample_rows - 2] + 1
+    rows = torch.cat([torch.tensor([0, w.M - 1]), inner]).sort().values
+    return rows.to(torch.int64)
