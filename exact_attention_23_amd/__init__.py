@@ -1,0 +1,123 @@
+"""Python binding of libfa2 (exact attention forward pass on gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libfa2.so``.  PyTorch is used for device memory and streams.
+There is no CPU fallback: if the library is missing, importing the binding
+raises.
+
+``fa2_fwd`` mirrors the C entry point of ``include/fa2.h`` one to one (raw
+device pointers and sizes).  ``forward`` is the tensor-level convenience that
+allocates ``o`` and ``lse`` with torch and calls ``fa2_fwd`` on the current
+stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["FA2_DTYPE_F32", "FA2_DTYPE_BF16", "FA2_OK", "FA2_ERR_INVALID_ARGUMENT",
+           "FA2_ERR_UNSUPPORTED", "FA2_ERR_LAUNCH", "FA2_ERR_NO_DEVICE", "Fa2Error",
+           "fa2_fwd", "fa2_status_string", "forward", "library_path", "EXPORTED_SYMBOLS"]
+
+FA2_DTYPE_F32 = 0
+FA2_DTYPE_BF16 = 1
+
+FA2_OK = 0
+FA2_ERR_INVALID_ARGUMENT = 1
+FA2_ERR_UNSUPPORTED = 2
+FA2_ERR_LAUNCH = 3
+FA2_ERR_NO_DEVICE = 4
+
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_status_string")
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfa2.so")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -m exact_attention_23_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.fa2_fwd.restype = ctypes.c_int
+    lib.fa2_fwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+    ]
+    lib.fa2_status_string.restype = ctypes.c_char_p
+    lib.fa2_status_string.argtypes = [ctypes.c_int]
+    return lib
+
+
+_lib = _load()
+
+
+class Fa2Error(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(fa2_status_string(status))
+
+
+def fa2_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, M: int, N: int, D: int,
+            scale: float, causal: int, dtype: int, stream: int | None) -> int:
+    """Direct call of the C entry point; pointers are integers (device
+    addresses).  Returns the fa2_status code."""
+    return int(_lib.fa2_fwd(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream))
+
+
+def fa2_status_string(status: int) -> str:
+    return _lib.fa2_status_string(int(status)).decode()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return FA2_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return FA2_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Attention forward on the current CUDA/HIP stream.
+
+    q: [B,H,M,D], k/v: [B,H,N,D] contiguous device tensors of one dtype
+    (float32 or bfloat16).  Returns (o [B,H,M,D] in q's dtype, lse [B,H,M]
+    float32).  ``scale`` defaults to 1/sqrt(D).
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D tensor")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, H, M, D = q.shape
+    N = k.shape[2]
+    if k.shape != (B, H, N, D) or v.shape != (B, H, N, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse is None:
+        lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, M) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B,H,M]")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, H, M, N, D, float(scale), int(bool(causal)), _dtype_code(q), stream)
+    if st != FA2_OK:
+        raise Fa2Error(st)
+    return out, lse

@@ -1,0 +1,99 @@
+/*
+ * fa2.h -- C ABI of libfa2: exact attention forward pass for AMD gfx950.
+ *
+ * The operation (all four pages agree on it):
+ *
+ *   O[b,h,i,:] = sum_j P[i,j] * V[b,h,j,:],
+ *   P[i,j]     = exp(S[i,j] - L[b,h,i]),   S[i,j] = scale * <Q[b,h,i,:], K[b,h,j,:]>,
+ *   L[b,h,i]   = log sum_{j visible} exp(S[i,j])  (natural log of the scaled scores)
+ *
+ * i.e. O = softmax(scale * Q K^T) V, optionally causal, plus the per-row
+ * logsumexp L = m + log(l) of the online softmax.  Sources:
+ *  - "From FlashAttention to FlashAttention 2", section "Background:
+ *    FlashAttention 1" (the definition of standard attention) and section
+ *    "Backward Pass: Recomputation" (L = m + log(l) is stored per row);
+ *  - "FlashAttention-2 from PyTorch to Triton", opening description of the
+ *    forward pass and of the second output L;
+ *  - "Writing FlashAttention 2 in Triton", Step 1 (grid over Q tiles and
+ *    batch*head), Step 4 (causal visibility: key <= query) and Step 6 (the
+ *    wrapper's [B,H,N,D] tensors and fp32 L of shape [B,H,N_Q]);
+ *  - "From FlashAttention to FlashAttention 2", section "Layer 2: C++ Entry
+ *    Point" (dispatch on dtype, head dimension and causal onto a stream).
+ * The M x N score matrix is never materialised: the kernels stream K/V tiles
+ * and keep the running max m, sum l and unnormalised O in registers.
+ */
+#ifndef FA2_H_
+#define FA2_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o.  lse is always float32. */
+typedef enum {
+    FA2_DTYPE_F32 = 0,  /* IEEE binary32 */
+    FA2_DTYPE_BF16 = 1  /* bfloat16 (1-8-7); o is rounded to nearest-even */
+} fa2_dtype;
+
+typedef enum {
+    FA2_OK = 0,
+    FA2_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad scale */
+    FA2_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement (e.g. D) */
+    FA2_ERR_LAUNCH = 3,           /* the HIP runtime refused the launch */
+    FA2_ERR_NO_DEVICE = 4         /* no usable gfx950 device for the current context */
+} fa2_status;
+
+/*
+ * fa2_fwd -- attention forward pass on one HIP stream.
+ *
+ * Layout: every tensor is a contiguous row-major device array.
+ *   q   [B, H, M, D]   element type `dtype`
+ *   k   [B, H, N, D]   element type `dtype`
+ *   v   [B, H, N, D]   element type `dtype`
+ *   o   [B, H, M, D]   element type `dtype` (output)
+ *   lse [B, H, M]      float32 (output): natural-log logsumexp of the scaled
+ *                      scores of each query row over its visible keys
+ * Q and K/V lengths may differ (cross-attention), as the pages' wrappers
+ * allow ("Writing FlashAttention 2 in Triton", bug catalogue on separate
+ * Q and KV strides).
+ *
+ * Arguments:
+ *   B, H   batch and heads, >= 0 (the kernels see only the product B*H)
+ *   M      query rows per head, >= 0
+ *   N      key/value rows per head, >= 1
+ *   D      head dimension; this build supports D = 64 and D = 128
+ *   scale  multiplier of Q K^T, finite and > 0 (callers pass 1/sqrt(D) for
+ *          standard attention)
+ *   causal 0: every key is visible; 1: key j is visible to query i iff
+ *          j <= i (top-left aligned, also when M != N)
+ *   dtype  a fa2_dtype value
+ *   stream a hipStream_t, or NULL for the null stream of the current device
+ *
+ * Ownership: all buffers are allocated and owned by the caller on the
+ * current HIP device; the library allocates nothing and keeps no state, so
+ * concurrent calls on different streams are safe.  o must not overlap q, k or
+ * v, and lse must not overlap any other buffer.
+ *
+ * Alignment: q, k, v, o must be 16-byte aligned, lse 4-byte aligned.
+ *
+ * Errors: all argument checks run before any HIP call; on failure nothing is
+ * launched and the outputs are untouched.  M == 0 or B*H == 0 returns FA2_OK
+ * without a launch.  On success one kernel is enqueued on `stream` and the
+ * call returns without synchronising; faults inside the kernel surface at
+ * the caller's next synchronisation.  FA2_ERR_LAUNCH is returned when the
+ * runtime rejects the launch.
+ */
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+            float scale, int causal, int dtype, void* stream);
+
+/* Static, NUL-terminated description of a fa2_status value. */
+const char* fa2_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H_ */

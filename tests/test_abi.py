@@ -1,0 +1,117 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+Every argument check of fa2_fwd runs before any HIP call, so invalid calls
+can be exercised with fake pointers on a machine without a GPU.  Nothing
+here launches a kernel.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_23_amd as fa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2.h")
+
+A = 0x10000  # fake, 16-byte aligned, non-overlapping "device" addresses
+Q, K, V, O, L = A, 2 * A, 3 * A, 4 * A, 5 * A
+
+
+def call(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, M=16, N=16, D=64, scale=0.125, causal=0,
+         dtype=fa2.FA2_DTYPE_F32):
+    return fa2.fa2_fwd(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, None)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa2_\w+)\s*\(", text)))
+
+
+def test_header_declares_exactly_the_exported_symbols():
+    assert declared_functions() == sorted(fa2.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", fa2.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, f"{name} declared in fa2.h but not exported"
+    lib = ctypes.CDLL(fa2.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name)
+
+
+def test_library_is_built_for_gfx950_only(tmp_path):
+    llvm = "/opt/rocm/llvm/bin"
+    if not os.path.exists(os.path.join(llvm, "clang-offload-bundler")):
+        pytest.skip("ROCm LLVM tools unavailable")
+    fatbin = tmp_path / "fatbin.bin"
+    subprocess.run([os.path.join(llvm, "llvm-objcopy"), f"--dump-section=.hip_fatbin={fatbin}",
+                    fa2.library_path(), str(tmp_path / "copy.so")], check=True)
+    out = subprocess.run([os.path.join(llvm, "clang-offload-bundler"), "--list", "--type=o",
+                          f"--input={fatbin}"], capture_output=True, text=True, check=True)
+    targets = [t for t in out.stdout.split() if "amdgcn" in t]
+    assert targets and all(t.endswith("gfx950") for t in targets), targets
+
+
+def test_status_strings():
+    for st in (fa2.FA2_OK, fa2.FA2_ERR_INVALID_ARGUMENT, fa2.FA2_ERR_UNSUPPORTED,
+               fa2.FA2_ERR_LAUNCH, fa2.FA2_ERR_NO_DEVICE):
+        s = fa2.fa2_status_string(st)
+        assert s.startswith("FA2_")
+    assert "unknown" in fa2.fa2_status_string(99)
+
+
+@pytest.mark.parametrize("kw", [dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(lse=0)])
+def test_null_pointers_rejected(kw):
+    assert call(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(H=-2), dict(M=-1), dict(N=0), dict(N=-5),
+                                dict(D=0), dict(D=-64)])
+def test_bad_sizes_rejected(kw):
+    assert call(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, float("inf"), float("nan")])
+def test_bad_scale_rejected(scale):
+    assert call(scale=scale) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=2), dict(dtype=-1), dict(causal=2), dict(causal=-1)])
+def test_bad_enums_rejected(kw):
+    assert call(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(q=Q + 8), dict(k=K + 4), dict(v=V + 2), dict(o=O + 8), dict(lse=L + 2)])
+def test_misaligned_pointers_rejected(kw):
+    assert call(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("D", [16, 32, 96, 256, 65])
+def test_unsupported_head_dim(D):
+    assert call(D=D) == fa2.FA2_ERR_UNSUPPORTED
+    assert call(D=D, dtype=fa2.FA2_DTYPE_BF16) == fa2.FA2_ERR_UNSUPPORTED
+
+
+def test_oversized_head_rejected_before_launch():
+    assert call(M=1 << 25, D=64) == fa2.FA2_ERR_UNSUPPORTED
+    assert call(N=1 << 25, D=128) == fa2.FA2_ERR_UNSUPPORTED
+
+
+def test_overlapping_outputs_rejected():
+    # o overlapping q, and lse inside o
+    assert call(o=Q) == fa2.FA2_ERR_INVALID_ARGUMENT
+    assert call(lse=O + 16) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(M=0), dict(B=0), dict(H=0)])
+def test_empty_problem_is_a_no_op(kw):
+    # returns before touching the HIP runtime, so this is safe without a GPU
+    assert call(**kw) == fa2.FA2_OK
+    assert call(dtype=fa2.FA2_DTYPE_BF16, causal=1, D=128, **kw) == fa2.FA2_OK

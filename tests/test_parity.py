@@ -1,0 +1,152 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Tolerances (max-abs over every checked element, O and L separately):
+  fp32 I/O: 1e-4 on O and on L;
+  bf16 I/O: 2e-2 on O and 1e-3 on L,
+where the oracle consumes exactly the bf16-rounded inputs the kernel sees.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.golden_cases import build_case, load_cases
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-3)}
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(q, k, v, causal, scale=None):
+    import exact_attention_23_amd as fa2
+    dq, dk, dv = (t.to("cuda") for t in (q, k, v))
+    o, lse = fa2.forward(dq, dk, dv, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def compare(o, lse, o_ref, l_ref, dtype, what):
+    tol_o, tol_l = TOL[dtype]
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), f"{what}: non-finite output"
+    err_o = float(np.abs(o - o_ref).max()) if o.size else 0.0
+    err_l = float(np.abs(lse - l_ref).max()) if lse.size else 0.0
+    note(f"{what}: max|dO|={err_o:.3e} (tol {tol_o}), max|dL|={err_l:.3e} (tol {tol_l})")
+    assert err_o <= tol_o, f"{what}: O error {err_o} > {tol_o}"
+    assert err_l <= tol_l, f"{what}: L error {err_l} > {tol_l}"
+    return err_o, err_l
+
+
+def check_case(B, H, M, N, D, dtype, causal, seed=0, qk_sigma=1.0, v_sigma=1.0, rows=None):
+    what = f"B={B} H={H} M={M} N={N} D={D} {dtype} causal={causal} seed={seed}"
+    note("case " + what)
+    q, k, v = workloads.make_inputs(B, H, M, N, D, dtype, seed, qk_sigma, v_sigma)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = run_gpu(q, k, v, causal)
+    o_ref, l_ref = oracle.attention(q, k, v, scale, causal, rows=rows)
+    if rows is not None:
+        o, lse = o[:, :, rows], lse[:, :, rows]
+    return compare(o, lse, o_ref, l_ref, dtype, what)
+
+
+# ------------------------------------------------------------- the workloads
+
+@pytest.mark.parametrize("name", workloads.ORDER)
+def test_workload_parity(name):
+    w = workloads.get(name)
+    rows = workloads.sample_rows(w)
+    rows = None if rows is None else rows.numpy()
+    check_case(w.B, w.H, w.M, w.N, w.D, w.dtype, w.causal, w.seed, w.qk_sigma, w.v_sigma, rows=rows)
+
+
+# ------------------------------------------- the pages' harness shapes, ragged
+
+# (batch, n_queries, n_keys) of the Triton test harness, run at D in {64, 128}
+HARNESS = [(4, 128, 128), (2, 1024, 1024), (2, 100, 100), (1, 37, 53), (1, 200, 96)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B,M,N", HARNESS)
+def test_harness_shapes(B, M, N, D, causal, dtype):
+    check_case(B, 2, M, N, D, dtype, causal, seed=M + N + D)
+
+
+# sizes around the 128-row query tile and the 64/32-key K/V tiles
+EDGES = [(1, 1), (1, 300), (300, 1), (31, 33), (63, 65), (64, 64), (65, 63), (127, 129),
+         (128, 128), (129, 127), (255, 257), (257, 255), (1000, 3000), (3000, 1000)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("M,N", EDGES)
+def test_tile_edges(M, N, causal, dtype):
+    D = 128 if (M + N) % 2 else 64
+    check_case(1, 3, M, N, D, dtype, causal, seed=7 * M + N)
+
+
+# the shape sweep of the Triton numerics harness (causal bf16), trimmed to
+# what the oracle finishes in seconds
+@pytest.mark.parametrize("B,H,N,D", [(1, 8, 512, 64), (1, 8, 2048, 64), (1, 4, 4096, 128)])
+def test_numerics_sweep(B, H, N, D):
+    check_case(B, H, N, N, D, "bf16", True, seed=N + D)
+
+
+def test_large_magnitude_scores_bf16_and_f32():
+    # scores with std ~16 and maxima past the fp32 exp overflow point
+    check_case(2, 2, 333, 777, 64, "bf16", False, seed=11, qk_sigma=4.0)
+    check_case(2, 2, 333, 777, 128, "f32", True, seed=12, qk_sigma=3.0)
+
+
+# ------------------------------------------------------ closed-form examples
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", load_cases(), ids=lambda c: c["name"])
+def test_golden_worked_examples(case, dtype):
+    q, k, v, scale, causal, o_exp, l_exp = build_case(case)
+    td = workloads.torch_dtype(dtype)
+    tq, tk, tv = (torch.from_numpy(x).to(td) for x in (q, k, v))
+    # the examples use values exact in bf16, so both dtypes see the same inputs
+    assert torch.equal(tq.float(), torch.from_numpy(q)) and torch.equal(tv.float(), torch.from_numpy(v))
+    o, lse = run_gpu(tq, tk, tv, causal, scale)
+    compare(o, lse, o_exp, l_exp, dtype, case["name"] + " " + dtype)
+    if dtype == "bf16" and "o_bf16_rne" in case:
+        # exact tie: round-to-nearest-even is the only admissible result
+        assert np.all(o == case["o_bf16_rne"]), np.unique(o)
+
+
+# ---------------------------------------------------------------- properties
+
+def test_rows_independent_of_batching():
+    # each (b,h) slice gives bitwise the result it gives alone
+    import exact_attention_23_amd as fa2
+    q, k, v = workloads.make_inputs(2, 3, 200, 150, 128, "bf16", seed=21)
+    dq, dk, dv = (t.cuda() for t in (q, k, v))
+    o, lse = fa2.forward(dq, dk, dv, causal=True)
+    for b, h in [(0, 0), (1, 2)]:
+        o1, l1 = fa2.forward(dq[b:b + 1, h:h + 1].contiguous(), dk[b:b + 1, h:h + 1].contiguous(),
+                             dv[b:b + 1, h:h + 1].contiguous(), causal=True)
+        assert torch.equal(o[b, h], o1[0, 0]) and torch.equal(lse[b, h], l1[0, 0])
+
+
+def test_runs_on_a_side_stream():
+    import exact_attention_23_amd as fa2
+    q, k, v = workloads.make_inputs(1, 4, 256, 256, 64, "f32", seed=22)
+    dq, dk, dv = (t.cuda() for t in (q, k, v))
+    ref_o, ref_l = fa2.forward(dq, dk, dv)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o, lse = fa2.forward(dq, dk, dv)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
