@@ -1,0 +1,302 @@
+"""Benchmark of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one fa2_fwd call over one batch of the workload (all of its heads
+and query rows), inputs already resident in HBM.  The default workload is the
+fp32 shape the CUDA project page benchmarks (B=4, H=12, M=N=2048, D=64,
+non-causal).  Prints ONE JSON line with the whole-job throughput
+(4*B*H*M*N*D flop per step, halved for causal) and:
+
+* roofline: the kernel's achieved TFLOP/s = counted flop per launch / mean
+  launch duration (HIP events on the launch stream over the timed region),
+  against MI355X's dense MFMA peak for the dtype; traffic = HBM bytes per
+  launch from the committed rocprofv3 counter summary, when it was taken on
+  the current kernel source;
+* cpu_baseline: the CPU oracle timed on this host on the same workload;
+* workloads: per-launch latency (median of 100 after 25 warm-ups, with and
+  without an L2/MALL flush before each launch) of every workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("attention fwd TFLOP/s (4·B·H·M·N·D) and % of MFMA peak; "
+          "latency µs, 1 MI355X")
+# MI355X dense matrix peaks (AMD's published figures): bf16 2.5 PFLOP/s
+# (256 CU x 2.4 GHz x 4096 flop/clk), fp32 157.3 TFLOP/s.
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+# Context only: the CUDA project page's hand-written fp32 kernel on an RTX 4080
+# at B=4,H=12,M=N=2048,D=64 took 3810.30 us, i.e. 13.53 TFLOP/s by this count.
+PAGE_REFERENCE_US = {"mha_f32_2k": 3810.30}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_23_amd", "csrc", "fa2_fwd.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were
+    taken on the kernel source that is built now."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get("workloads", {}).get(workload)
+    if not entry or data.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def time_launches(fn, stream, warmup: int, reps: int, flush=None):
+    """Per-launch durations (ms) from HIP events recorded on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        times.append((s, e))
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in times]
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def cpu_baseline(w):
+    """The fp64 oracle, as it stands, on the whole workload (one pass)."""
+    import oracle
+    import workloads
+    q, k, v = workloads.workload_inputs(w)
+    rows = workloads.sample_rows(w)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, w.scale, w.causal, rows=None if rows is None else rows.numpy())
+    dt = time.perf_counter() - t0
+    flops = w.flops if rows is None else w.flops * len(rows) / w.M  # approximate for sampled rows
+    sample = (f"all {w.B}x{w.H}x{w.M} query rows of {w.name}, one pass" if rows is None else
+              f"{len(rows)} sampled rows per head of {w.name}")
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": dt}
+
+
+COPY_BYTES = 256 * 1024 * 1024
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES, five times: under
+    rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE per dispatch give the counter
+    reading for a known number of HBM bytes read and written."""
+    import torch
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 5}), flush=True)
+    return 0
+
+
+def _read_counter_csv(path, counter):
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload, out=TRAFFIC_FILE):
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch)
+    into HBM bytes per launch of the attention kernel, each counter scaled by
+    its reading for the plain copy of COPY_BYTES (copy_calibration)."""
+    def med_for(rows, pred):
+        vals = [v for name, v in rows if pred(name)]
+        if not vals:
+            raise ValueError("no matching dispatches")
+        return median(vals), len(vals)
+
+    is_fa2 = lambda n: "fa2_fwd_" in n
+    is_copy = lambda n: "copyBuffer" in n or "copy" in n.lower()
+    cf, _ = med_for(_read_counter_csv(copy_fetch_csv, "FETCH_SIZE"), is_copy)
+    cw, _ = med_for(_read_counter_csv(copy_write_csv, "WRITE_SIZE"), is_copy)
+    f, nf = med_for(_read_counter_csv(fetch_csv, "FETCH_SIZE"), is_fa2)
+    wr, nw = med_for(_read_counter_csv(write_csv, "WRITE_SIZE"), is_fa2)
+    fetch_scale = COPY_BYTES / (cf * 1024.0)
+    write_scale = COPY_BYTES / (cw * 1024.0)
+    entry = {"fetch_bytes": f * 1024.0 * fetch_scale, "write_bytes": wr * 1024.0 * write_scale,
+             "fetch_kib_raw": f, "write_kib_raw": wr, "fetch_scale": fetch_scale,
+             "write_scale": write_scale, "dispatches": [nf, nw]}
+    entry["bytes_per_launch"] = entry["fetch_bytes"] + entry["write_bytes"]
+    try:
+        with open(out) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        data = {}
+    if data.get("kernel_source_sha256") != kernel_source_hash():
+        data = {"kernel_source_sha256": kernel_source_hash(), "workloads": {}}
+    data["workloads"][workload] = entry
+    with open(out, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({workload: entry}), flush=True)
+    return 0
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--workload", default="mha_f32_2k")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (calibrates HBM counters)")
+    ap.add_argument("--summarize-counters", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic.json for --workload from rocprofv3 counter CSVs")
+    args = ap.parse_args(argv)
+
+    if args.copy_calibration:
+        return copy_calibration()
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters, workload=args.workload)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the forward pass shards over batch*head with no exchange, "
+                                   "but multi-GPU runs are not part of it)"}), flush=True)
+        return 2
+
+    import torch
+    import exact_attention_23_amd as fa2
+    import workloads
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def setup(w):
+        q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.M), dtype=torch.float32, device=dev)
+        return q, k, v, o, lse
+
+    def launcher(w, bufs):
+        q, k, v, o, lse = bufs
+        code = fa2.FA2_DTYPE_F32 if w.dtype == "f32" else fa2.FA2_DTYPE_BF16
+        args_ = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 w.B, w.H, w.M, w.N, w.D, w.scale, int(w.causal), code, stream.cuda_stream)
+
+        def fn():
+            st = fa2.fa2_fwd(*args_)
+            if st != fa2.FA2_OK:
+                raise fa2.Fa2Error(st)
+        return fn
+
+    w = workloads.get(args.workload)
+    bufs = setup(w)
+    fn = launcher(w, bufs)
+
+    # ---- the timed steps: W untimed, then exactly K, synchronised on both sides
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        events.append((s, e))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in events]
+    ms_per_step = wall * 1e3 / args.steps
+    mean_launch_ms = sum(launch_ms) / len(launch_ms)
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+
+    achieved = w.flops / (mean_launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name),
+                "mean_launch_us": round(mean_launch_ms * 1e3, 2),
+                "kernel": f"fa2_fwd_{w.dtype}_kernel (D={w.D}, causal={int(w.causal)})"}
+
+    ref_us = PAGE_REFERENCE_US.get(w.name)
+    vs_baseline = None if ref_us is None else round(value / (w.flops / (ref_us * 1e-6) / 1e12), 3)
+
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": vs_baseline,
+        "dtype": w.dtype, "data": "synthetic (seeded Gaussian Q/K/V)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "M": w.M, "N": w.N, "D": w.D,
+                   "causal": w.causal, "io_dtype": w.dtype, "global_batch": w.B, "seq_len": w.M,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+    }
+    del bufs
+
+    # ---- per-workload latency table (each launch timed alone)
+    if not args.no_extras:
+        flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        table = {}
+        for name in workloads.ORDER:
+            wx = workloads.get(name)
+            bx = setup(wx)
+            fx = launcher(wx, bx)
+            hot = time_launches(fx, stream, 25, 100)
+            cold = time_launches(fx, stream, 3, 20, flush=flush_buf.zero_)
+            us, us_cold = median(hot) * 1e3, median(cold) * 1e3
+            tf = wx.flops / (us * 1e-6) / 1e12
+            table[name] = {"shape": f"B={wx.B},H={wx.H},M={wx.M},N={wx.N},D={wx.D}",
+                           "dtype": wx.dtype, "causal": wx.causal,
+                           "us_median": round(us, 2), "us_median_l2_flushed": round(us_cold, 2),
+                           "tflops": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK_TFLOPS[wx.dtype], 4),
+                           "hbm_gbs_compulsory": round(wx.compulsory_bytes / (us * 1e-6) / 1e9, 1)}
+            del bx, fx
+        del flush_buf
+        result["workloads"] = table
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
