@@ -39,12 +39,35 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+def _hip_runtimes_mapped():
+    """Distinct HIP runtime library files mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) >= 6 and "libamdhip64" in parts[-1]:
+                    paths.add(os.path.realpath(parts[-1]))
+    except OSError:
+        pass
+    return paths
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
             f"{_LIB_PATH} is not built; run `python -m exact_attention_23_amd.build` "
             "(there is no fallback implementation)")
+    # Device memory and streams come from torch, so libfa2 must bind to torch's
+    # HIP runtime.  Importing torch first makes the loader resolve libfa2's
+    # libamdhip64.so.7 dependency to the copy torch already mapped; loading
+    # libfa2 first would map a second, different HIP runtime into the process.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(_LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError("two different HIP runtimes are loaded in this process "
+                          f"({sorted(runtimes)}); import torch before loading libfa2")
     lib.fa2_fwd.restype = ctypes.c_int
     lib.fa2_fwd.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,

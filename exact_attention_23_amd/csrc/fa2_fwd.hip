@@ -35,13 +35,13 @@
 //    per-row rescale factor alpha lives in the same lane as the O^T column it
 //    scales, so no cross-lane traffic is needed for the rescale either.
 //  * P leaves the S^T accumulator already in the B-operand layout of the PV
-//    MFMA (lane = query, 8 keys per lane).  The A operand, V^T, is read from
-//    an LDS copy of V stored transposed ([d][key]) with bits 2 and 3 of the key
-//    index swapped, which makes the 8 keys a lane needs contiguous: one 16-byte
-//    LDS read per MFMA operand.
-//  * K and V^T tiles are double-buffered in LDS with padded rows (bank-conflict
-//    free 16-byte reads; conflict-free transposing 4-byte writes); the next
-//    tile's global loads are issued before the current tile's MFMAs.
+//    MFMA (lane = query, 8 keys per lane).  The A operand, V^T, is read from a
+//    row-major LDS copy of V with ds_read_b64_tr_b16 (bf16), or one key per
+//    lane with plain reads (fp32).
+//  * bf16: K and V tiles are copied global -> LDS by the load unit
+//    (global_load_lds_dwordx4) into XOR-swizzled rows and double-buffered;
+//    fp32: staged through VGPRs into padded rows.  Either way the next tile's
+//    loads are issued before the current tile's MFMAs, one barrier per tile.
 //  * Q stays in VGPRs for the whole K/V loop; O^T, m, l stay in registers.
 //  * Causal grids launch the heaviest query tiles first; batch*head is the
 //    fastest-varying grid index so that all tiles of one head land on the same
@@ -57,6 +57,7 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -67,12 +68,6 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // half h (= lane / 32); the column is lane % 32.
 __device__ __forceinline__ constexpr int acc_row(int r, int h) {
     return 8 * (r >> 2) + 4 * h + (r & 3);
-}
-
-// Position of key `key` (tile-local) in the transposed V tile: bits 2 and 3
-// swapped, so that the 8 keys one lane feeds to a PV MFMA are adjacent.
-__device__ __forceinline__ constexpr int vperm(int key) {
-    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
 __device__ __forceinline__ float xchg_half(float x) {
@@ -97,6 +92,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ---------------------------------------------------------------------------
 // D: head dim (64 or 128); BN: keys per K/V tile (multiple of 32);
 // NW: waves per workgroup; QB: 32-query blocks per wave.
+//
+// K and V tiles are copied global -> LDS by the load unit itself
+// (global_load_lds_dwordx4: each lane moves one 16-byte chunk, a wave fills
+// 1 KiB of LDS), so no VGPRs stage them.  Rows are stored unpadded with their
+// 16-byte chunks XOR-permuted per row (the lane -> global address map does the
+// permutation), which keeps both read patterns free of bank conflicts:
+//  * K is read as the A operand of S^T = K Q^T: lanes 0..31 read 32 different
+//    key rows at one logical chunk -> chunk ^= f_K(row) spreads them;
+//  * V is read with ds_read_b64_tr_b16, which hands each lane 4 consecutive
+//    keys of one d column (a 4-key x 16-d block per 16 lanes transposed in
+//    flight) -- exactly the A operand of O^T += V^T P^T -- so V needs no
+//    transposition in LDS; chunk ^= f_V(row) keeps the 4 rows x 64 bytes a
+//    half-wave reads in distinct banks.
 template <int D, int BN, int NW, int QB>
 struct Bf16Traits {
     static constexpr int kThreads = NW * 64;
@@ -105,28 +113,51 @@ struct Bf16Traits {
     static constexpr int kKB = BN / 32;           // 32-key blocks per tile
     static constexpr int kDB = D / 32;            // 32-wide d blocks of O^T
     static constexpr int kDS = D / 16;            // MFMA k-steps of S^T
-    static constexpr int kKStr = D + 8;           // K tile row stride (elements)
-    static constexpr int kVStr = BN + 8;          // V^T tile row stride (elements)
-    static constexpr int kKElems = BN * kKStr;
-    static constexpr int kVElems = D * kVStr;
-    static constexpr int kKChunks = BN * D / 8;   // 16-byte chunks per K tile
-    static constexpr int kVPairs = (BN / 2) * (D / 8);  // (key pair, 8-d chunk) items
-    static constexpr int kKPerThread = kKChunks / kThreads;
-    static constexpr int kVPerThread = kVPairs / kThreads;
-    static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
-    static_assert(kKChunks % kThreads == 0 && kVPairs % kThreads == 0, "loader split");
-    static constexpr size_t kLdsBytes = 2 * (kKElems + kVElems) * sizeof(__bf16);
+    static constexpr int kCPR = D / 8;            // 16-byte chunks per row
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kTileBytes = BN * kRowBytes;
+    static constexpr int kTileChunks = BN * kCPR;
+    static constexpr int kLoadsPerWave = kTileChunks / (64 * NW);  // per tensor per tile
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(BN % 32 == 0, "key tile");
+    static_assert(kTileChunks % (64 * NW) == 0, "loader split");
+    static constexpr size_t kLdsBytes = 4 * (size_t)kTileBytes;  // K, V double-buffered
 };
 
+// XOR applied to the 16-byte chunk index of LDS row r (K tile): the 16 rows a
+// quarter-wave reads at one logical chunk land in 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+// XOR for the V tile: rows key0..key0+3 (key0 % 4 == 0) read 64 bytes each at
+// one set of 4 logical chunks; the XOR moves each row's 64 bytes to its own
+// quarter of the 256-byte bank space.
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
 template <int D, int BN, int NW, int QB, bool CAUSAL>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64, 2)
 fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     const __bf16* __restrict__ V, __bf16* __restrict__ O,
                     float* __restrict__ LSE, int BH, int M, int N, int n_qt,
                     float c_log2) {
     using T = Bf16Traits<D, BN, NW, QB>;
-    __shared__ __attribute__((aligned(16))) __bf16 sK[2][T::kKElems];
-    __shared__ __attribute__((aligned(16))) __bf16 sV[2][T::kVElems];
+    // Two K/V tile buffers, each BN rows x D bf16 (rows unpadded, chunks
+    // swizzled).  They are separate arrays, and the loop below is unrolled by
+    // two so every access names its buffer statically: the compiler can then
+    // see that the asynchronous copy into one buffer never aliases the reads
+    // of the other, and does not stall those reads on the copy.
+    __shared__ __attribute__((aligned(1024))) char sK0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK1[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV1[T::kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -146,7 +177,6 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* Kh = K + (int64_t)bh * N * D;
     const __bf16* Vh = V + (int64_t)bh * N * D;
 
-    // K/V tiles covered by this workgroup, and by this wave
     const int kv_end = CAUSAL ? min(N, q0 + T::kBM) : N;
     const int n_kv = (kv_end + BN - 1) / BN;
     int n_kv_wave = n_kv;
@@ -168,180 +198,213 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         }
     }
 
-    // ---- running state (fp32): O^T accumulators, max (log2 units), partial sum
+    // Running state per query row (one row per lane): O^T accumulators, the
+    // max m (log2 units), and two partial sums of this lane's weights: l_run
+    // over the bf16-rounded weights the PV MFMA consumed (the denominator of
+    // O), l_exact over the fp32 weights (for L = m + log l).
     floatx16 oacc[T::kDB][QB];
-    float m_run[QB], l_run[QB];
+    float m_run[QB], l_run[QB], l_exact[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m_run[qb] = -INFINITY;
         l_run[qb] = 0.f;
+        l_exact[qb] = 0.f;
 #pragma unroll
         for (int db = 0; db < T::kDB; ++db) oacc[db][qb] = floatx16{};
     }
 
-    // ---- tile loader: global -> registers -> LDS
-    u32x4 kreg[T::kKPerThread];
-    u32x4 vreg[T::kVPerThread][2];
-
-    auto load_tile = [&](int kt) {
+    // ---- async tile copy: wave w moves chunks [w*L*64, (w+1)*L*64) of each
+    // tensor's tile; LDS slot s holds row s / CPR, physical chunk s % CPR,
+    // i.e. logical chunk (s % CPR) ^ swz(row).  Keys past N are clamped to
+    // row N-1 (finite data whose scores are masked to -inf).
+    auto issue_tile = [&](int kt, char* kdst, char* vdst) {
         const int kbase = kt * BN;
 #pragma unroll
-        for (int i = 0; i < T::kKPerThread; ++i) {
-            const int id = tid + i * T::kThreads;
-            const int row = id / (D / 8);
-            const int c8 = id % (D / 8);
-            const int key = kbase + row;
-            kreg[i] = key < N ? *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + 8 * c8)
-                              : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < T::kVPerThread; ++i) {
-            const int id = tid + i * T::kThreads;
-            const int a2 = id % (BN / 2);
-            const int c8 = id / (BN / 2);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int key = kbase + 2 * a2 + j;
-                vreg[i][j] = key < N ? *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + 8 * c8)
-                                     : u32x4{0, 0, 0, 0};
-            }
+        for (int i = 0; i < T::kLoadsPerWave; ++i) {
+            const int slot0 = (wave * T::kLoadsPerWave + i) * 64;
+            const int slot = slot0 + lane;
+            const int r = slot / T::kCPR;
+            const int p = slot % T::kCPR;
+            const int key = min(kbase + r, N - 1);
+            const __bf16* ksrc = Kh + (int64_t)key * D + 8 * (p ^ swz_k<D>(r));
+            const __bf16* vsrc = Vh + (int64_t)key * D + 8 * (p ^ swz_v<D>(r));
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)ksrc,
+                                             (__attribute__((address_space(3))) void*)(kdst + slot0 * 16),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)vsrc,
+                                             (__attribute__((address_space(3))) void*)(vdst + slot0 * 16),
+                                             16, 0, 0);
         }
     };
 
-    auto store_tile = [&](int buf) {
+    // per-lane parts of the LDS fragment addresses
+    // K (A operand of S^T): row 32 kb + l32, logical chunk 2 s + h.
+    int k_lane_off[T::kDS];
 #pragma unroll
-        for (int i = 0; i < T::kKPerThread; ++i) {
-            const int id = tid + i * T::kThreads;
-            const int row = id / (D / 8);
-            const int c8 = id % (D / 8);
-            *reinterpret_cast<u32x4*>(&sK[buf][row * T::kKStr + 8 * c8]) = kreg[i];
-        }
+    for (int s = 0; s < T::kDS; ++s)
+        k_lane_off[s] = l32 * T::kRowBytes + 16 * ((2 * s + h) ^ swz_k<D>(l32));
+    // V^T (A operand of O^T += V^T P^T) via ds_read_b64_tr_b16: lane
+    // 16 g + 4 t + a reads row key0 + t, d = d0 + 4a, where the 16-lane group g
+    // covers d0 = 32 db + 16 (g & 1) and key0 = ... + 4 (g >> 1).
+    const int vg = lane >> 4, vt = (lane >> 2) & 3, va = lane & 3;
+    const int v_row_lane = 4 * (vg >> 1) + vt;
+    int v_lane_off[T::kDB];
 #pragma unroll
-        for (int i = 0; i < T::kVPerThread; ++i) {
-            const int id = tid + i * T::kThreads;
-            const int a2 = id % (BN / 2);
-            const int c8 = id / (BN / 2);
-            const int col = vperm(2 * a2);  // keys 2*a2 and 2*a2+1 stay adjacent
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t w0 = vreg[i][0][e >> 1];
-                const uint32_t w1 = vreg[i][1][e >> 1];
-                const uint32_t packed = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                                : ((w0 & 0xffffu) | (w1 << 16));
-                *reinterpret_cast<uint32_t*>(&sV[buf][(8 * c8 + e) * T::kVStr + col]) = packed;
-            }
-        }
-    };
-
-    if (n_kv > 0) {
-        load_tile(0);
-        store_tile(0);
+    for (int db = 0; db < T::kDB; ++db) {
+        const int c = 4 * db + 2 * (vg & 1) + (va >> 1);
+        v_lane_off[db] = v_row_lane * T::kRowBytes + 16 * (c ^ swz_v<D>(v_row_lane)) + 8 * (va & 1);
     }
-    __syncthreads();
 
-    for (int kt = 0; kt < n_kv; ++kt) {
-        const int buf = kt & 1;
-        const bool has_next = kt + 1 < n_kv;
-        if (has_next) load_tile(kt + 1);
-
-        if (kt < n_kv_wave) {
-            const __bf16* kt_lds = sK[buf];
-            const __bf16* vt_lds = sV[buf];
-
-            // S^T = K Q^T for BN keys x QPW queries
-            floatx16 sacc[T::kKB][QB];
+    auto compute_tile = [&](int kt, const char* klds, const char* vlds) {
+        // S^T = K Q^T for BN keys x QPW queries; K fragments are read one
+        // k-step ahead of the MFMAs that use them.
+        floatx16 sacc[T::kKB][QB];
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = floatx16{};
+        bf16x8 kf[2][T::kKB];
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+            kf[0][kb] = *reinterpret_cast<const bf16x8*>(klds + 32 * kb * T::kRowBytes + k_lane_off[0]);
+#pragma unroll
+        for (int s = 0; s < T::kDS; ++s) {
+            if (s + 1 < T::kDS) {
+#pragma unroll
+                for (int kb = 0; kb < T::kKB; ++kb)
+                    kf[(s + 1) & 1][kb] = *reinterpret_cast<const bf16x8*>(
+                        klds + 32 * kb * T::kRowBytes + k_lane_off[s + 1]);
+            }
+            // keep the next step's reads ahead of this step's MFMAs
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = floatx16{};
-#pragma unroll
-            for (int s = 0; s < T::kDS; ++s) {
-#pragma unroll
-                for (int kb = 0; kb < T::kKB; ++kb) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-                        kt_lds + (32 * kb + l32) * T::kKStr + 16 * s + 8 * h);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], sacc[kb][qb], 0, 0, 0);
-                }
-            }
+                for (int qb = 0; qb < QB; ++qb)
+                    sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][kb], qf[qb][s], sacc[kb][qb], 0, 0, 0);
+        }
 
-            // boundary tiles only: keys past N, and (causal) keys after the query
-            const int kbase = kt * BN;
-            const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > qw0);
-            if (need_mask) {
+        // boundary tiles only: keys past N, and (causal) keys after the query
+        const int kbase = kt * BN;
+        const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > qw0);
+        if (need_mask) {
 #pragma unroll
-                for (int kb = 0; kb < T::kKB; ++kb)
+            for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        const int query = qw0 + 32 * qb + l32;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = kbase + 32 * kb + acc_row(r, h);
-                            const bool vis = key < N && (!CAUSAL || key <= query);
-                            if (!vis) sacc[kb][qb][r] = -INFINITY;
-                        }
-                    }
-            }
-
-            // online softmax (log2 domain); P overwrites S in place
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < T::kKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
-                mx = fmaxf(mx, xchg_half(mx));
-                const float m_new = fmaxf(m_run[qb], mx * c_log2);
-                // a row with no visible key so far keeps exp2 arguments finite
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = fast_exp2(m_run[qb] - m_use);
-                m_run[qb] = m_new;
-                float lsum = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < T::kKB; ++kb)
+                for (int qb = 0; qb < QB; ++qb) {
+                    const int query = qw0 + 32 * qb + l32;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float p = fast_exp2(fmaf(sacc[kb][qb][r], c_log2, -m_use));
-                        sacc[kb][qb][r] = p;
-                        lsum += p;
+                        const int key = kbase + 32 * kb + acc_row(r, h);
+                        const bool vis = key < N && (!CAUSAL || key <= query);
+                        if (!vis) sacc[kb][qb][r] = -INFINITY;
                     }
-                l_run[qb] = fmaf(l_run[qb], alpha, lsum);
+                }
+        }
+
+        bf16x8 pf[T::kKB][2][QB];  // P^T as B operands of the PV MFMAs
+        // Online softmax in the log2 domain.  The running max is only moved
+        // (and O, l rescaled) when some row's max grew by more than 8 (a factor
+        // 256); otherwise P = exp2(s*c - m_run) <= 256, which the fp32 O and l
+        // and the bf16 P hold as accurately -- O / l and m + log2 l are the
+        // same quantities either way.
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2)
+                    mx = fmaxf(mx, fmaxf(sacc[kb][qb][r], sacc[kb][qb][r + 1]));
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            const float m_tile = mx * c_log2;
+            if (__any(m_tile > m_run[qb] + 8.f)) {
+                const float m_new = fmaxf(m_run[qb], m_tile);
+                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run[qb] - m_new);
+                m_run[qb] = m_new;
+                l_run[qb] *= alpha;
+                l_exact[qb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < T::kDB; ++db) oacc[db][qb] *= alpha;
             }
-
-            // O^T += V^T P^T: two 16-key MFMA steps per 32-key block
+            // P is rounded to bf16 once, for the PV MFMA.  l_run sums exactly
+            // those rounded weights (two per v_dot2 against (1, 1)), so O / l_run
+            // is a true weighted mean of V rows; l_exact sums the fp32 weights,
+            // which L needs to within 1e-3.
+            const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+            float lsum = 0.f, esum = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < T::kKB; ++kb) {
+            for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
-                for (int ms = 0; ms < 2; ++ms) {
-                    bf16x8 pf[QB];
+                for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                        for (int t = 0; t < 8; ++t) pf[qb][t] = (__bf16)sacc[kb][qb][8 * ms + t];
-#pragma unroll
-                    for (int db = 0; db < T::kDB; ++db) {
-                        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-                            vt_lds + (32 * db + l32) * T::kVStr + 32 * kb + 16 * ms + 8 * h);
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb)
-                            oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], oacc[db][qb], 0, 0, 0);
+                    for (int t = 0; t < 8; t += 2) {
+                        const float p0 = fast_exp2(fmaf(sacc[kb][qb][8 * ms + t], c_log2, -m_use));
+                        const float p1 = fast_exp2(fmaf(sacc[kb][qb][8 * ms + t + 1], c_log2, -m_use));
+                        const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+                        pf[kb][ms][qb][t] = pp[0];
+                        pf[kb][ms][qb][t + 1] = pp[1];
+                        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, lsum, false);
+                        esum += p0;
+                        esum += p1;
                     }
-                }
-            }
+            l_run[qb] += lsum;
+            l_exact[qb] += esum;
         }
 
-        if (has_next) store_tile(buf ^ 1);
+        // O^T += V^T P^T: two 16-key MFMA steps per 32-key block; each A
+        // operand is two transposed 4-key reads, issued one step ahead.
+        constexpr int kSteps = T::kKB * 2;
+        auto read_v = [&](int step, int db) {
+            const char* p0 = vlds + 16 * step * T::kRowBytes + v_lane_off[db];
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 8 * T::kRowBytes));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 vf[2][T::kDB];
+#pragma unroll
+        for (int db = 0; db < T::kDB; ++db) vf[0][db] = read_v(0, db);
+#pragma unroll
+        for (int step = 0; step < kSteps; ++step) {
+            if (step + 1 < kSteps) {
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db) vf[(step + 1) & 1][db] = read_v(step + 1, db);
+            }
+            const int kb = step >> 1, ms = step & 1;
+#pragma unroll
+            for (int db = 0; db < T::kDB; ++db)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[step & 1][db], pf[kb][ms][qb], oacc[db][qb], 0, 0, 0);
+        }
+    };
+
+    // ---- main loop, unrolled by two over the buffer pair
+    if (n_kv > 0) issue_tile(0, sK0, sV0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < n_kv; kt += 2) {
+        if (kt + 1 < n_kv) issue_tile(kt + 1, sK1, sV1);
+        if (kt < n_kv_wave) compute_tile(kt, sK0, sV0);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
+        __syncthreads();
+        if (kt + 1 >= n_kv) break;
+        if (kt + 2 < n_kv) issue_tile(kt + 2, sK0, sV0);
+        if (kt + 1 < n_kv_wave) compute_tile(kt + 1, sK1, sV1);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
     // ---- epilogue: one normalisation, L = (m + log2 l) * ln 2, RNE store
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const float l_tot = l_run[qb] + xchg_half(l_run[qb]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[qb]), __float_as_uint(l_run[qb]), false, false);
+        const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const auto se = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_exact[qb]), __float_as_uint(l_exact[qb]), false, false);
+        const float l_ex = __uint_as_float(se[0]) + __uint_as_float(se[1]);
         const int query = qw0 + 32 * qb + l32;
         if (query < M) {
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -356,7 +419,7 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     w[1] = pack_bf16x2(oacc[db][qb][4 * g + 2] * inv, oacc[db][qb][4 * g + 3] * inv);
                     *reinterpret_cast<uint2*>(orow + d) = make_uint2(w[0], w[1]);
                 }
-            if (h == 0) LSE[(int64_t)bh * M + query] = (m_run[qb] + fast_log2(l_tot)) * kLn2;
+            if (h == 0) LSE[(int64_t)bh * M + query] = (m_run[qb] + fast_log2(l_ex)) * kLn2;
         }
     }
 }

@@ -76,6 +76,11 @@ typedef enum {
  * concurrent calls on different streams are safe.  o must not overlap q, k or
  * v, and lse must not overlap any other buffer.
  *
+ * Runtime: libfa2 needs libamdhip64.so.7.  In a process that already uses a
+ * HIP runtime (for instance the copy bundled with PyTorch), load that runtime
+ * before libfa2 so both share one runtime: pointers and streams from one HIP
+ * runtime are meaningless to another.
+ *
  * Alignment: q, k, v, o must be 16-byte aligned, lse 4-byte aligned.
  *
  * Errors: all argument checks run before any HIP call; on failure nothing is

@@ -115,3 +115,10 @@ def test_empty_problem_is_a_no_op(kw):
     # returns before touching the HIP runtime, so this is safe without a GPU
     assert call(**kw) == fa2.FA2_OK
     assert call(dtype=fa2.FA2_DTYPE_BF16, causal=1, D=128, **kw) == fa2.FA2_OK
+
+
+def test_single_hip_runtime_in_process():
+    # The binding must share torch's HIP runtime: pointers and streams come
+    # from torch.  A second runtime copy would make every launch fail.
+    import torch  # noqa: F401
+    assert len(fa2._hip_runtimes_mapped()) <= 1, fa2._hip_runtimes_mapped()

@@ -41,9 +41,6 @@ def call(q, k, v, o, lse, causal, dtype_code):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("M,N,D", [(1, 1, 64), (100, 37, 128), (129, 200, 64), (1000, 3000, 64), (300, 300, 128)])
 def test_no_out_of_bounds_access(M, N, D, causal, dtype):
-    if (M, N, D, causal, dtype) == (100, 37, 128, False, "f32"):
-        pytest.skip("the host process segfaulted at the start of this case (inside torch, "
-                    "before its library call) in one GPU session; cause not identified yet")
     B, H = 2, 3
     q, k, v = workloads.make_inputs(B, H, M, N, D, dtype, seed=M + N)
     code = fa2.FA2_DTYPE_F32 if dtype == "f32" else fa2.FA2_DTYPE_BF16
