@@ -49,6 +49,7 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <type_traits>
 #include <stdint.h>
 #include <string.h>
 
@@ -79,12 +80,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo;  // round to nearest even
-    __bf16 b = (__bf16)hi;
-    uint16_t ua, ub;
-    __builtin_memcpy(&ua, &a, 2);
-    __builtin_memcpy(&ub, &b, 2);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
+    // one v_cvt_pk_bf16_f32: both halves rounded to nearest even
+    const __bf16 __attribute__((ext_vector_type(2))) v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -217,21 +215,29 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // tensor's tile; LDS slot s holds row s / CPR, physical chunk s % CPR,
     // i.e. logical chunk (s % CPR) ^ swz(row).  Keys past N are clamped to
     // row N-1 (finite data whose scores are masked to -inf).
+    int cp_row[T::kLoadsPerWave], cp_kcol[T::kLoadsPerWave], cp_vcol[T::kLoadsPerWave];
+#pragma unroll
+    for (int i = 0; i < T::kLoadsPerWave; ++i) {
+        const int slot = (wave * T::kLoadsPerWave + i) * 64 + lane;
+        const int r = slot / T::kCPR, p = slot % T::kCPR;
+        cp_row[i] = r;
+        cp_kcol[i] = 16 * (p ^ swz_k<D>(r));  // byte offsets within the row
+        cp_vcol[i] = 16 * (p ^ swz_v<D>(r));
+    }
+    const char* Kb = reinterpret_cast<const char*>(Kh);
+    const char* Vb = reinterpret_cast<const char*>(Vh);
     auto issue_tile = [&](int kt, char* kdst, char* vdst) {
         const int kbase = kt * BN;
+        const bool tail = kbase + BN > N;  // only the last tile can run past N
 #pragma unroll
         for (int i = 0; i < T::kLoadsPerWave; ++i) {
             const int slot0 = (wave * T::kLoadsPerWave + i) * 64;
-            const int slot = slot0 + lane;
-            const int r = slot / T::kCPR;
-            const int p = slot % T::kCPR;
-            const int key = min(kbase + r, N - 1);
-            const __bf16* ksrc = Kh + (int64_t)key * D + 8 * (p ^ swz_k<D>(r));
-            const __bf16* vsrc = Vh + (int64_t)key * D + 8 * (p ^ swz_v<D>(r));
-            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)ksrc,
+            const int key = tail ? min(kbase + cp_row[i], N - 1) : kbase + cp_row[i];
+            const uint32_t row_off = (uint32_t)key * (uint32_t)T::kRowBytes;
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(Kb + (row_off + cp_kcol[i])),
                                              (__attribute__((address_space(3))) void*)(kdst + slot0 * 16),
                                              16, 0, 0);
-            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)vsrc,
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(Vb + (row_off + cp_vcol[i])),
                                              (__attribute__((address_space(3))) void*)(vdst + slot0 * 16),
                                              16, 0, 0);
         }
@@ -255,7 +261,8 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         v_lane_off[db] = v_row_lane * T::kRowBytes + 16 * (c ^ swz_v<D>(v_row_lane)) + 8 * (va & 1);
     }
 
-    auto compute_tile = [&](int kt, const char* klds, const char* vlds) {
+    auto compute_tile = [&](auto mask_tag, int kt, const char* klds, const char* vlds) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         // S^T = K Q^T for BN keys x QPW queries; K fragments are read one
         // k-step ahead of the MFMAs that use them.
         floatx16 sacc[T::kKB][QB];
@@ -284,22 +291,22 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][kb], qf[qb][s], sacc[kb][qb], 0, 0, 0);
         }
 
-        // boundary tiles only: keys past N, and (causal) keys after the query
-        const int kbase = kt * BN;
-        const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > qw0);
-        if (need_mask) {
+        // boundary tiles only: keys past N, and (causal) keys after the
+        // query.  Key kbase + 32 kb + acc_row(r, h) is visible iff its
+        // compile-time part 32 kb + 8 (r / 4) + r % 4 is <= lim.
+        if constexpr (MASK) {
+            const int kbase = kt * BN;
 #pragma unroll
-            for (int kb = 0; kb < T::kKB; ++kb)
+            for (int qb = 0; qb < QB; ++qb) {
+                int lim = N - 1 - kbase;
+                if (CAUSAL) lim = min(lim, qw0 + 32 * qb + l32 - kbase);
+                lim -= 4 * h;
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const int query = qw0 + 32 * qb + l32;
+                for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kbase + 32 * kb + acc_row(r, h);
-                        const bool vis = key < N && (!CAUSAL || key <= query);
-                        if (!vis) sacc[kb][qb][r] = -INFINITY;
-                    }
-                }
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][qb][r] = -INFINITY;
+            }
         }
 
         bf16x8 pf[T::kKB][2][QB];  // P^T as B operands of the PV MFMAs
@@ -310,18 +317,23 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         // same quantities either way.
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
+            // IEEE maximum (v_maximum3_f32): no NaN quieting of each input
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; r += 2)
-                    mx = fmaxf(mx, fmaxf(sacc[kb][qb][r], sacc[kb][qb][r + 1]));
+                    mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(sacc[kb][qb][r], sacc[kb][qb][r + 1]));
             {
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
             }
             const float m_tile = mx * c_log2;
             if (__any(m_tile > m_run[qb] + 8.f)) {
+                // (the empty volatile asm keeps the compiler from turning this
+                // rarely taken branch into an always-executed multiply by a
+                // selected factor)
+                __asm__ volatile("");
                 const float m_new = fmaxf(m_run[qb], m_tile);
                 const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run[qb] - m_new);
                 m_run[qb] = m_new;
@@ -386,14 +398,24 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     if (n_kv > 0) issue_tile(0, sK0, sV0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // A tile needs masking if it runs past N or (causal) reaches past the
+    // wave's first query row; all other tiles take the mask-free path.
+    auto run_tile = [&](int kt, const char* klds, const char* vlds) {
+        if (kt >= n_kv_wave) return;
+        const int kbase = kt * BN;
+        if (kbase + BN > N || (CAUSAL && kbase + BN - 1 > qw0))
+            compute_tile(std::true_type{}, kt, klds, vlds);
+        else
+            compute_tile(std::false_type{}, kt, klds, vlds);
+    };
     for (int kt = 0; kt < n_kv; kt += 2) {
         if (kt + 1 < n_kv) issue_tile(kt + 1, sK1, sV1);
-        if (kt < n_kv_wave) compute_tile(kt, sK0, sV0);
+        run_tile(kt, sK0, sV0);
         __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
         __syncthreads();
         if (kt + 1 >= n_kv) break;
         if (kt + 2 < n_kv) issue_tile(kt + 2, sK0, sV0);
-        if (kt + 1 < n_kv_wave) compute_tile(kt + 1, sK1, sV1);
+        run_tile(kt + 1, sK1, sV1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
