@@ -44,8 +44,15 @@ KERNEL_SRC = os.path.join(ROOT, "exact_attention_23_amd", "csrc", "fa2_fwd.hip")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 of the kernel source with comments and blank space removed, so
+    that counters stay attached to the code they were taken on."""
+    import re
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = "\n".join(" ".join(line.split()) for line in src.splitlines() if line.strip())
+    return hashlib.sha256(src.encode()).hexdigest()
 
 
 def load_traffic(workload: str):

@@ -46,6 +46,9 @@
 //  * Causal grids launch the heaviest query tiles first; batch*head is the
 //    fastest-varying grid index so that all tiles of one head land on the same
 //    XCD (workgroups are dealt to the 8 XCDs round-robin).
+//  * bf16 at D = 128 uses a ping-pong schedule between two groups of four
+//    waves (see fa2_fwd_bf16_pp_kernel), because a wave's own MFMA and VALU
+//    work does not overlap on gfx950 while two waves on one SIMD do.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -140,8 +143,8 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 __device__ constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-template <int D, int BN, int NW, int QB, bool CAUSAL>
-__global__ void __launch_bounds__(NW * 64, 2)
+template <int D, int BN, int NW, int QB, int WAVES_PER_SIMD, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64, WAVES_PER_SIMD)
 fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     const __bf16* __restrict__ V, __bf16* __restrict__ O,
                     float* __restrict__ LSE, int BH, int M, int N, int n_qt,
@@ -447,6 +450,331 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 }
 
 // ---------------------------------------------------------------------------
+// bf16 kernel, ping-pong schedule
+// ---------------------------------------------------------------------------
+// On gfx950 a wave's own MFMA and VALU instructions do not overlap, but the
+// MFMA of one wave and the VALU of another wave on the same SIMD do.  This
+// kernel therefore runs two groups of four waves (waves w and w + 4 share a
+// SIMD) half a tile out of phase, separated by workgroup barriers:
+//
+//   period:     0        1        2          3          4 ...
+//   group A:  S(0)     sm(0)    PV(0)+S(1)  sm(1)      PV(1)+S(2)
+//   group B:  -        S(0)     sm(0)      PV(0)+S(1)  sm(1)
+//
+// where S(t) = K_t Q^T and PV(t) = O^T += V_t^T P_t^T are MFMA-only phases and
+// sm(t) (mask, online softmax, rescale) is VALU-only, so while one wave of a
+// SIMD keeps the matrix core busy the other wave uses the vector ALU.
+//
+// K_t is read in periods 2t (A) and 2t+1 (B), V_t in 2t+2 (A) and 2t+3 (B).
+// At the start of each even period 2t every wave issues its share of the
+// copies of K_{t+1} and V_t; it waits for them before the barrier that ends
+// period 2t+1, one period before they are read.  K_t and V_t live in buffer
+// t % 2; the loop is unrolled over four periods so that every LDS access
+// names its buffer statically and the compiler can see that the copies in
+// flight never alias the buffers being read.
+//
+// Each wave owns 32 query rows; group A takes the even 32-row blocks of the
+// workgroup's 256 rows and group B the odd ones, so under a causal mask the
+// two waves of a SIMD need the same number of tiles (to within one).
+template <int D, int BN>
+struct PPTraits {
+    static constexpr int kNW = 8;
+    static constexpr int kThreads = kNW * 64;
+    static constexpr int kBM = 32 * kNW;          // query rows per workgroup
+    static constexpr int kKB = BN / 32;           // 32-key blocks per tile
+    static constexpr int kDB = D / 32;            // 32-wide d blocks of O^T
+    static constexpr int kDS = D / 16;            // MFMA k-steps of S^T
+    static constexpr int kCPR = D / 8;            // 16-byte chunks per row
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kTileBytes = BN * kRowBytes;
+    static constexpr int kTileChunks = BN * kCPR;
+    static constexpr int kLoadsPerWave = kTileChunks / (64 * kNW);  // per tensor per tile
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(BN % 32 == 0, "key tile");
+    static_assert(kTileChunks % (64 * kNW) == 0, "loader split");
+};
+
+template <int D, int BN, bool CAUSAL>
+__global__ void __launch_bounds__(512, 2)
+fa2_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                       const __bf16* __restrict__ V, __bf16* __restrict__ O,
+                       float* __restrict__ LSE, int BH, int M, int N, int n_qt,
+                       float c_log2) {
+    using T = PPTraits<D, BN>;
+    __shared__ __attribute__((aligned(1024))) char sK0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK1[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV1[T::kTileBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int grp = wave >> 2;  // 0: group A, 1: group B
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+
+    // workgroup -> (batch*head, query tile); causal: heaviest tiles first
+    const int wg = blockIdx.x;
+    const int bh = wg % BH;
+    int qt = wg / BH;
+    if (CAUSAL) qt = n_qt - 1 - qt;
+    const int q0 = qt * T::kBM;
+    const int qw0 = q0 + 32 * (2 * (wave & 3) + grp);  // first query row of this wave
+
+    const __bf16* Qh = Q + (int64_t)bh * M * D;
+    const __bf16* Kh = K + (int64_t)bh * N * D;
+    const __bf16* Vh = V + (int64_t)bh * N * D;
+
+    const int kv_end = CAUSAL ? min(N, q0 + T::kBM) : N;
+    const int n_kv = (kv_end + BN - 1) / BN;
+    int n_w = n_kv;  // tiles this wave needs
+    if (CAUSAL) n_w = min(n_kv, (min(N, qw0 + 32) + BN - 1) / BN);
+    if (qw0 >= M) n_w = 0;
+
+    // ---- Q fragments: B operand of S^T = K Q^T (lane = query, 8 d values)
+    bf16x8 qf[T::kDS];
+    {
+        const int row = qw0 + l32;
+#pragma unroll
+        for (int s = 0; s < T::kDS; ++s)
+            qf[s] = row < M ? *reinterpret_cast<const bf16x8*>(Qh + (int64_t)row * D + 16 * s + 8 * h)
+                            : bf16x8{};
+    }
+
+    // Running state of this lane's query row: O^T, the max m (log2 units),
+    // l_run over the bf16-rounded weights the PV MFMA consumed (denominator of
+    // O) and l_exact over the fp32 weights (for L).
+    floatx16 oacc[T::kDB];
+#pragma unroll
+    for (int db = 0; db < T::kDB; ++db) oacc[db] = floatx16{};
+    float m_run = -INFINITY, l_run = 0.f, l_exact = 0.f;
+    floatx16 sacc[T::kKB];        // S^T of the tile between its S and sm phases
+    bf16x8 pf[T::kKB][2];         // P^T of the tile between its sm and PV phases
+#pragma unroll
+    for (int kb = 0; kb < T::kKB; ++kb) pf[kb][0] = pf[kb][1] = bf16x8{};
+
+    // ---- async copies (global_load_lds), per-lane constant parts
+    int cp_row[T::kLoadsPerWave], cp_kcol[T::kLoadsPerWave], cp_vcol[T::kLoadsPerWave];
+#pragma unroll
+    for (int i = 0; i < T::kLoadsPerWave; ++i) {
+        const int slot = (wave * T::kLoadsPerWave + i) * 64 + lane;
+        const int r = slot / T::kCPR, p = slot % T::kCPR;
+        cp_row[i] = r;
+        cp_kcol[i] = 16 * (p ^ swz_k<D>(r));
+        cp_vcol[i] = 16 * (p ^ swz_v<D>(r));
+    }
+    const char* Kb = reinterpret_cast<const char*>(Kh);
+    const char* Vb = reinterpret_cast<const char*>(Vh);
+    auto issue_copy = [&](const char* src, const int* cp_col, int kt, char* dst) {
+        const int kbase = kt * BN;
+        const bool tail = kbase + BN > N;
+#pragma unroll
+        for (int i = 0; i < T::kLoadsPerWave; ++i) {
+            const int slot0 = (wave * T::kLoadsPerWave + i) * 64;
+            const int key = tail ? min(kbase + cp_row[i], N - 1) : kbase + cp_row[i];
+            const uint32_t row_off = (uint32_t)key * (uint32_t)T::kRowBytes;
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + (row_off + cp_col[i])),
+                                             (__attribute__((address_space(3))) void*)(dst + slot0 * 16),
+                                             16, 0, 0);
+        }
+    };
+
+    // ---- per-lane parts of the LDS fragment addresses
+    int k_lane_off[T::kDS];
+#pragma unroll
+    for (int s = 0; s < T::kDS; ++s)
+        k_lane_off[s] = l32 * T::kRowBytes + 16 * ((2 * s + h) ^ swz_k<D>(l32));
+    const int vg = lane >> 4, vt = (lane >> 2) & 3, va = lane & 3;
+    const int v_row_lane = 4 * (vg >> 1) + vt;
+    int v_lane_off[T::kDB];
+#pragma unroll
+    for (int db = 0; db < T::kDB; ++db) {
+        const int c = 4 * db + 2 * (vg & 1) + (va >> 1);
+        v_lane_off[db] = v_row_lane * T::kRowBytes + 16 * (c ^ swz_v<D>(v_row_lane)) + 8 * (va & 1);
+    }
+
+    // ---- MFMA phase: PV(t-1) and S(t), interleaved so that consecutive
+    // MFMAs never feed the same accumulator (4 O^T blocks + 2 S^T blocks).
+    // Operand fragments are read from LDS two steps ahead of their MFMAs
+    // (the scheduling fences keep the compiler from sinking the reads next
+    // to their uses).  PV(-1) multiplies a zero P by a zero-filled V buffer;
+    // the S(n_w) of a wave's last MFMA phase is computed and discarded, so
+    // every phase runs the same straight-line code.
+    constexpr int kSteps = T::kDS * T::kKB;  // == number of PV MFMAs
+    static_assert(kSteps == T::kKB * 2 * T::kDB, "one PV and one S MFMA per step");
+    auto read_v = [&](const char* vprev, int i) {
+        const int step = i / T::kDB, db = i % T::kDB;
+        const char* p0 = vprev + 16 * step * T::kRowBytes + v_lane_off[db];
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 8 * T::kRowBytes));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto read_k = [&](const char* klds, int i) {
+        const int s = i / T::kKB, kb = i % T::kKB;
+        return *reinterpret_cast<const bf16x8*>(klds + 32 * kb * T::kRowBytes + k_lane_off[s]);
+    };
+    auto mfma_phase = [&](int t, const char* klds, const char* vprev) {
+        if (t > n_w) return;
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb) sacc[kb] = floatx16{};
+        constexpr int kAhead = 2;
+        bf16x8 vr[kAhead + 1], kr[kAhead + 1];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) {
+            vr[i] = read_v(vprev, i);
+            kr[i] = read_k(klds, i);
+        }
+#pragma unroll
+        for (int i = 0; i < kSteps; ++i) {
+            if (i + kAhead < kSteps) {
+                vr[(i + kAhead) % (kAhead + 1)] = read_v(vprev, i + kAhead);
+                kr[(i + kAhead) % (kAhead + 1)] = read_k(klds, i + kAhead);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                const int step = i / T::kDB, db = i % T::kDB;
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % (kAhead + 1)], pf[step >> 1][step & 1],
+                                                                   oacc[db], 0, 0, 0);
+            }
+            {
+                const int s = i / T::kKB, kb = i % T::kKB;
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % (kAhead + 1)], qf[s], sacc[kb], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- VALU phase: mask (boundary tiles), online softmax, rescale.
+    // The running max only moves when some row's max grew by more than 8 (a
+    // factor 256); otherwise P = exp2(s*c - m_run) <= 256, which the fp32 O
+    // and l and the bf16 P hold as accurately.  P is rounded to bf16 once;
+    // l_run sums those rounded weights (two per v_dot2 against (1, 1)) so
+    // O / l_run is a true weighted mean of V rows, and l_exact sums the fp32
+    // weights for L.
+    auto valu_phase = [&](int t) {
+        if (t < 0 || t >= n_w) return;
+        const int kbase = t * BN;
+        if (kbase + BN > N || (CAUSAL && kbase + BN - 1 > qw0)) {
+            __asm__ volatile("");  // keep this a branch, not a select per element
+            int lim = N - 1 - kbase;
+            if (CAUSAL) lim = min(lim, qw0 + l32 - kbase);
+            lim -= 4 * h;
+#pragma unroll
+            for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+        }
+        // row max as four independent v_maximum3 chains, then a short tree
+        float mxp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float& m4 = mxp[((kb * 16 + r) >> 1) & 3];
+                m4 = __builtin_elementwise_maximum(m4, __builtin_elementwise_maximum(sacc[kb][r], sacc[kb][r + 1]));
+            }
+        float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mxp[0], mxp[1]),
+                                                 __builtin_elementwise_maximum(mxp[2], mxp[3]));
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float m_tile = mx * c_log2;
+        if (__any(m_tile > m_run + 8.f)) {
+            __asm__ volatile("");
+            const float m_new = fmaxf(m_run, m_tile);
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+            l_exact *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::kDB; ++db) oacc[db] *= alpha;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        // partial sums in four independent chains each (no serial add chain)
+        float lsum[4] = {0.f, 0.f, 0.f, 0.f}, esum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                for (int u = 0; u < 8; u += 2) {
+                    const int c = (u >> 1) & 3;
+                    const float p0 = fast_exp2(fmaf(sacc[kb][8 * ms + u], c_log2, -m_use));
+                    const float p1 = fast_exp2(fmaf(sacc[kb][8 * ms + u + 1], c_log2, -m_use));
+                    const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+                    pf[kb][ms][u] = pp[0];
+                    pf[kb][ms][u + 1] = pp[1];
+                    lsum[c] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, lsum[c], false);
+                    esum[c] += p0 + p1;
+                }
+        l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+        l_exact += (esum[0] + esum[1]) + (esum[2] + esum[3]);
+    };
+
+    // ---- prologue: K_0 in buffer 0; V buffer 1 zeroed (read by PV(-1))
+    for (int i = tid; i < T::kTileBytes / 16; i += T::kThreads)
+        reinterpret_cast<uint4*>(sV1)[i] = make_uint4(0, 0, 0, 0);
+    if (n_kv > 0) issue_copy(Kb, cp_kcol, 0, sK0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ---- 2 n_kv + 2 periods, four per loop trip (two tiles)
+    const int n_periods = 2 * n_kv + 2;
+    for (int p0 = 0; p0 < n_periods; p0 += 4) {
+        const int t0 = p0 >> 1;  // even tile of this trip
+        // period p0: copies K_{t0+1} -> buf 1, V_{t0} -> buf 0.
+        //            A: PV(t0-1) [V buf 1] + S(t0) [K buf 0];  B: sm(t0-1)
+        if (t0 + 1 < n_kv) issue_copy(Kb, cp_kcol, t0 + 1, sK1);
+        if (t0 < n_kv) issue_copy(Vb, cp_vcol, t0, sV0);
+        if (grp == 0) mfma_phase(t0, sK0, sV1);
+        else valu_phase(t0 - 1);
+        __syncthreads();
+        // period p0+1: B: PV(t0-1) [V buf 1] + S(t0) [K buf 0];  A: sm(t0)
+        if (grp == 1) mfma_phase(t0, sK0, sV1);
+        else valu_phase(t0);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of K_{t0+1}, V_{t0}
+        __syncthreads();
+        // period p0+2: copies K_{t0+2} -> buf 0, V_{t0+1} -> buf 1.
+        //              A: PV(t0) [V buf 0] + S(t0+1) [K buf 1];  B: sm(t0)
+        if (t0 + 2 < n_kv) issue_copy(Kb, cp_kcol, t0 + 2, sK0);
+        if (t0 + 1 < n_kv) issue_copy(Vb, cp_vcol, t0 + 1, sV1);
+        if (grp == 0) mfma_phase(t0 + 1, sK1, sV0);
+        else valu_phase(t0);
+        __syncthreads();
+        // period p0+3: B: PV(t0) [V buf 0] + S(t0+1) [K buf 1];  A: sm(t0+1)
+        if (grp == 1) mfma_phase(t0 + 1, sK1, sV0);
+        else valu_phase(t0 + 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // ---- epilogue: one normalisation, L = (m + log2 l) * ln 2, RNE store
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+        const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const auto se = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_exact), __float_as_uint(l_exact), false, false);
+        const float l_ex = __uint_as_float(se[0]) + __uint_as_float(se[1]);
+        const int query = qw0 + l32;
+        if (query < M) {
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            __bf16* orow = O + ((int64_t)bh * M + query) * D;
+#pragma unroll
+            for (int db = 0; db < T::kDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d = 32 * db + 8 * g + 4 * h;
+                    const uint32_t w0 = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+                    const uint32_t w1 = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+                    *reinterpret_cast<uint2*>(orow + d) = make_uint2(w0, w1);
+                }
+            if (h == 0) LSE[(int64_t)bh * M + query] = (m_run + fast_log2(l_ex)) * kLn2;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel (v_mfma_f32_32x32x2_f32: true fp32 products, no reduced-precision
 // shortcut)
 // ---------------------------------------------------------------------------
@@ -662,7 +990,7 @@ struct LaunchArgs {
 
 typedef hipError_t (*launch_fn)(const LaunchArgs&, hipStream_t);
 
-template <int D, int BN, int NW, int QB, bool CAUSAL>
+template <int D, int BN, int NW, int QB, int WPS, bool CAUSAL>
 hipError_t launch_bf16(const LaunchArgs& a, hipStream_t stream) {
     using T = Bf16Traits<D, BN, NW, QB>;
     const int n_qt = (a.M + T::kBM - 1) / T::kBM;
@@ -674,7 +1002,23 @@ hipError_t launch_bf16(const LaunchArgs& a, hipStream_t stream) {
     int BH = a.BH, M = a.M, N = a.N;
     float c = a.c_log2;
     void* args[] = {&q, &k, &v, &o, &lse, &BH, &M, &N, (void*)&n_qt, &c};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fa2_fwd_bf16_kernel<D, BN, NW, QB, CAUSAL>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fa2_fwd_bf16_kernel<D, BN, NW, QB, WPS, CAUSAL>),
+                           dim3((unsigned)(n_qt * a.BH)), dim3(T::kThreads), args, 0, stream);
+}
+
+template <int D, int BN, bool CAUSAL>
+hipError_t launch_bf16_pp(const LaunchArgs& a, hipStream_t stream) {
+    using T = PPTraits<D, BN>;
+    const int n_qt = (a.M + T::kBM - 1) / T::kBM;
+    const __bf16* q = static_cast<const __bf16*>(a.q);
+    const __bf16* k = static_cast<const __bf16*>(a.k);
+    const __bf16* v = static_cast<const __bf16*>(a.v);
+    __bf16* o = static_cast<__bf16*>(a.o);
+    float* lse = a.lse;
+    int BH = a.BH, M = a.M, N = a.N;
+    float c = a.c_log2;
+    void* args[] = {&q, &k, &v, &o, &lse, &BH, &M, &N, (void*)&n_qt, &c};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fa2_fwd_bf16_pp_kernel<D, BN, CAUSAL>),
                            dim3((unsigned)(n_qt * a.BH)), dim3(T::kThreads), args, 0, stream);
 }
 
@@ -703,10 +1047,12 @@ struct Entry {
 };
 
 const Entry kTable[] = {
-    {FA2_DTYPE_BF16, 64, 0, &launch_bf16<64, 64, 4, 1, false>, 128},
-    {FA2_DTYPE_BF16, 64, 1, &launch_bf16<64, 64, 4, 1, true>, 128},
-    {FA2_DTYPE_BF16, 128, 0, &launch_bf16<128, 64, 4, 1, false>, 128},
-    {FA2_DTYPE_BF16, 128, 1, &launch_bf16<128, 64, 4, 1, true>, 128},
+    // bf16: 8 waves (two per SIMD) share each K/V tile; 256 query rows per
+    // workgroup; 64-key tiles at D=128, 128-key tiles at D=64 (measured best)
+    {FA2_DTYPE_BF16, 64, 0, &launch_bf16<64, 128, 8, 1, 2, false>, 256},
+    {FA2_DTYPE_BF16, 64, 1, &launch_bf16<64, 128, 8, 1, 2, true>, 256},
+    {FA2_DTYPE_BF16, 128, 0, &launch_bf16_pp<128, 64, false>, 256},
+    {FA2_DTYPE_BF16, 128, 1, &launch_bf16_pp<128, 64, true>, 256},
     {FA2_DTYPE_F32, 64, 0, &launch_f32<64, 64, 4, false>, 128},
     {FA2_DTYPE_F32, 64, 1, &launch_f32<64, 64, 4, true>, 128},
     {FA2_DTYPE_F32, 128, 0, &launch_f32<128, 32, 4, false>, 128},
