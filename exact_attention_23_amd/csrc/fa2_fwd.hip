@@ -38,10 +38,10 @@
 //    MFMA (lane = query, 8 keys per lane).  The A operand, V^T, is read from a
 //    row-major LDS copy of V with ds_read_b64_tr_b16 (bf16), or one key per
 //    lane with plain reads (fp32).
-//  * bf16: K and V tiles are copied global -> LDS by the load unit
-//    (global_load_lds_dwordx4) into XOR-swizzled rows and double-buffered;
-//    fp32: staged through VGPRs into padded rows.  Either way the next tile's
-//    loads are issued before the current tile's MFMAs, one barrier per tile.
+//  * bf16: K and V tiles are copied global -> LDS by the load unit (buffer
+//    loads with the LDS bit, 16 bytes per lane) into XOR-swizzled rows and
+//    double-buffered; fp32: staged through VGPRs into padded rows.  Either
+//    way the next tile's loads are issued before the current tile's MFMAs.
 //  * Q stays in VGPRs for the whole K/V loop; O^T, m, l stay in registers.
 //  * Causal grids launch the heaviest query tiles first; batch*head is the
 //    fastest-varying grid index so that all tiles of one head land on the same
@@ -67,6 +67,52 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
+
+// Buffer resource over `bytes` bytes at `base` (raw, no stride, dword data
+// format): loads past the end return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Workgroup barrier for LDS hand-offs between waves.  It waits for this
+// wave's own LDS operations only; __syncthreads would also drain every
+// outstanding global->LDS copy (its release fence covers global memory), which
+// forces copies issued for a later tile to land early.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt untouched
+    __asm__ volatile("s_barrier" ::: "memory");
+}
+
+// Copy of one BN-row K or V tile (rows kt*BN ...) of the head at `head` into
+// LDS by buffer loads, 16 bytes per lane per load.  `off` holds this lane's
+// kLoads byte offsets inside a tile
+// (row * row_bytes + swizzled chunk), fixed for the whole kernel; the tile
+// offset is a scalar and the LDS destination of a load is wave-uniform
+// (M0 + 16 * lane), so outside the last tile a copy costs no vector ALU work.
+// Rows past N re-read row N-1 (finite data; their scores are masked).
+template <int kLoads, int kRowBytes, int BN>
+__device__ __forceinline__ void copy_tile_to_lds(const void* head, const uint32_t* off,
+                                                 int wave_u, int kt, int N, char* dst) {
+    // the buffer covers one head's K (V): the range check backs up the clamp
+    const auto rsrc = make_rsrc(head, N * kRowBytes);
+    const int kbase = kt * BN;
+    const int soff = kbase * kRowBytes;
+    char* wdst = dst + wave_u * kLoads * 1024;
+    if (kbase + BN <= N) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(wdst + i * 1024),
+                                                     16, off[i], soff, 0, 0);
+    } else {
+        const uint32_t last = (uint32_t)(N - 1 - kbase);
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const uint32_t o = min(off[i] / kRowBytes, last) * kRowBytes + off[i] % kRowBytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(wdst + i * 1024),
+                                                     16, o, soff, 0, 0);
+        }
+    }
+}
 
 // Row of the 32x32 MFMA accumulator held in register r (0..15) by a lane in
 // half h (= lane / 32); the column is lane % 32.
@@ -95,8 +141,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // NW: waves per workgroup; QB: 32-query blocks per wave.
 //
 // K and V tiles are copied global -> LDS by the load unit itself
-// (global_load_lds_dwordx4: each lane moves one 16-byte chunk, a wave fills
-// 1 KiB of LDS), so no VGPRs stage them.  Rows are stored unpadded with their
+// (buffer_load_dwordx4 ... lds: each lane moves one 16-byte chunk, a wave
+// fills 1 KiB of LDS), so no VGPRs stage them.  Rows are stored unpadded with their
 // 16-byte chunks XOR-permuted per row (the lane -> global address map does the
 // permutation), which keeps both read patterns free of bank conflicts:
 //  * K is read as the A operand of S^T = K Q^T: lanes 0..31 read 32 different
@@ -216,34 +262,19 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
     // ---- async tile copy: wave w moves chunks [w*L*64, (w+1)*L*64) of each
     // tensor's tile; LDS slot s holds row s / CPR, physical chunk s % CPR,
-    // i.e. logical chunk (s % CPR) ^ swz(row).  Keys past N are clamped to
-    // row N-1 (finite data whose scores are masked to -inf).
-    int cp_row[T::kLoadsPerWave], cp_kcol[T::kLoadsPerWave], cp_vcol[T::kLoadsPerWave];
+    // i.e. logical chunk (s % CPR) ^ swz(row).
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t cp_koff[T::kLoadsPerWave], cp_voff[T::kLoadsPerWave];
 #pragma unroll
     for (int i = 0; i < T::kLoadsPerWave; ++i) {
         const int slot = (wave * T::kLoadsPerWave + i) * 64 + lane;
         const int r = slot / T::kCPR, p = slot % T::kCPR;
-        cp_row[i] = r;
-        cp_kcol[i] = 16 * (p ^ swz_k<D>(r));  // byte offsets within the row
-        cp_vcol[i] = 16 * (p ^ swz_v<D>(r));
+        cp_koff[i] = (uint32_t)(r * T::kRowBytes + 16 * (p ^ swz_k<D>(r)));
+        cp_voff[i] = (uint32_t)(r * T::kRowBytes + 16 * (p ^ swz_v<D>(r)));
     }
-    const char* Kb = reinterpret_cast<const char*>(Kh);
-    const char* Vb = reinterpret_cast<const char*>(Vh);
     auto issue_tile = [&](int kt, char* kdst, char* vdst) {
-        const int kbase = kt * BN;
-        const bool tail = kbase + BN > N;  // only the last tile can run past N
-#pragma unroll
-        for (int i = 0; i < T::kLoadsPerWave; ++i) {
-            const int slot0 = (wave * T::kLoadsPerWave + i) * 64;
-            const int key = tail ? min(kbase + cp_row[i], N - 1) : kbase + cp_row[i];
-            const uint32_t row_off = (uint32_t)key * (uint32_t)T::kRowBytes;
-            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(Kb + (row_off + cp_kcol[i])),
-                                             (__attribute__((address_space(3))) void*)(kdst + slot0 * 16),
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(Vb + (row_off + cp_vcol[i])),
-                                             (__attribute__((address_space(3))) void*)(vdst + slot0 * 16),
-                                             16, 0, 0);
-        }
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Kh, cp_koff, wave_u, kt, N, kdst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Vh, cp_voff, wave_u, kt, N, vdst);
     };
 
     // per-lane parts of the LDS fragment addresses
@@ -553,30 +584,18 @@ fa2_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
 #pragma unroll
     for (int kb = 0; kb < T::kKB; ++kb) pf[kb][0] = pf[kb][1] = bf16x8{};
 
-    // ---- async copies (global_load_lds), per-lane constant parts
-    int cp_row[T::kLoadsPerWave], cp_kcol[T::kLoadsPerWave], cp_vcol[T::kLoadsPerWave];
+    // ---- async tile copies (same chunk assignment as the kernel above)
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t cp_koff[T::kLoadsPerWave], cp_voff[T::kLoadsPerWave];
 #pragma unroll
     for (int i = 0; i < T::kLoadsPerWave; ++i) {
         const int slot = (wave * T::kLoadsPerWave + i) * 64 + lane;
         const int r = slot / T::kCPR, p = slot % T::kCPR;
-        cp_row[i] = r;
-        cp_kcol[i] = 16 * (p ^ swz_k<D>(r));
-        cp_vcol[i] = 16 * (p ^ swz_v<D>(r));
+        cp_koff[i] = (uint32_t)(r * T::kRowBytes + 16 * (p ^ swz_k<D>(r)));
+        cp_voff[i] = (uint32_t)(r * T::kRowBytes + 16 * (p ^ swz_v<D>(r)));
     }
-    const char* Kb = reinterpret_cast<const char*>(Kh);
-    const char* Vb = reinterpret_cast<const char*>(Vh);
-    auto issue_copy = [&](const char* src, const int* cp_col, int kt, char* dst) {
-        const int kbase = kt * BN;
-        const bool tail = kbase + BN > N;
-#pragma unroll
-        for (int i = 0; i < T::kLoadsPerWave; ++i) {
-            const int slot0 = (wave * T::kLoadsPerWave + i) * 64;
-            const int key = tail ? min(kbase + cp_row[i], N - 1) : kbase + cp_row[i];
-            const uint32_t row_off = (uint32_t)key * (uint32_t)T::kRowBytes;
-            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + (row_off + cp_col[i])),
-                                             (__attribute__((address_space(3))) void*)(dst + slot0 * 16),
-                                             16, 0, 0);
-        }
+    auto issue_copy = [&](const __bf16* head, const uint32_t* cp_off, int kt, char* dst) {
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(head, cp_off, wave_u, kt, N, dst);
     };
 
     // ---- per-lane parts of the LDS fragment addresses
@@ -716,7 +735,7 @@ fa2_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
     // ---- prologue: K_0 in buffer 0; V buffer 1 zeroed (read by PV(-1))
     for (int i = tid; i < T::kTileBytes / 16; i += T::kThreads)
         reinterpret_cast<uint4*>(sV1)[i] = make_uint4(0, 0, 0, 0);
-    if (n_kv > 0) issue_copy(Kb, cp_kcol, 0, sK0);
+    if (n_kv > 0) issue_copy(Kh, cp_koff, 0, sK0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -726,28 +745,28 @@ fa2_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
         const int t0 = p0 >> 1;  // even tile of this trip
         // period p0: copies K_{t0+1} -> buf 1, V_{t0} -> buf 0.
         //            A: PV(t0-1) [V buf 1] + S(t0) [K buf 0];  B: sm(t0-1)
-        if (t0 + 1 < n_kv) issue_copy(Kb, cp_kcol, t0 + 1, sK1);
-        if (t0 < n_kv) issue_copy(Vb, cp_vcol, t0, sV0);
+        if (t0 + 1 < n_kv) issue_copy(Kh, cp_koff, t0 + 1, sK1);
+        if (t0 < n_kv) issue_copy(Vh, cp_voff, t0, sV0);
         if (grp == 0) mfma_phase(t0, sK0, sV1);
         else valu_phase(t0 - 1);
-        __syncthreads();
+        lds_barrier();
         // period p0+1: B: PV(t0-1) [V buf 1] + S(t0) [K buf 0];  A: sm(t0)
         if (grp == 1) mfma_phase(t0, sK0, sV1);
         else valu_phase(t0);
         __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of K_{t0+1}, V_{t0}
-        __syncthreads();
+        lds_barrier();
         // period p0+2: copies K_{t0+2} -> buf 0, V_{t0+1} -> buf 1.
         //              A: PV(t0) [V buf 0] + S(t0+1) [K buf 1];  B: sm(t0)
-        if (t0 + 2 < n_kv) issue_copy(Kb, cp_kcol, t0 + 2, sK0);
-        if (t0 + 1 < n_kv) issue_copy(Vb, cp_vcol, t0 + 1, sV1);
+        if (t0 + 2 < n_kv) issue_copy(Kh, cp_koff, t0 + 2, sK0);
+        if (t0 + 1 < n_kv) issue_copy(Vh, cp_voff, t0 + 1, sV1);
         if (grp == 0) mfma_phase(t0 + 1, sK1, sV0);
         else valu_phase(t0);
-        __syncthreads();
+        lds_barrier();
         // period p0+3: B: PV(t0) [V buf 0] + S(t0+1) [K buf 1];  A: sm(t0+1)
         if (grp == 1) mfma_phase(t0 + 1, sK1, sV0);
         else valu_phase(t0 + 1);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- epilogue: one normalisation, L = (m + log2 l) * ln 2, RNE store
