@@ -5,10 +5,11 @@ kernels of ``libfa2.so``.  PyTorch is used for device memory and streams.
 There is no CPU fallback: if the library is missing, importing the binding
 raises.
 
-``fa2_fwd`` mirrors the C entry point of ``include/fa2.h`` one to one (raw
-device pointers and sizes).  ``forward`` is the tensor-level convenience that
-allocates ``o`` and ``lse`` with torch and calls ``fa2_fwd`` on the current
-stream.
+``fa2_fwd``, ``fa2_fwd_ex``, ``fa2_fwd_workspace_bytes`` and
+``fa2_fwd_num_splits`` mirror the C entry points of ``include/fa2.h`` one to
+one (raw device pointers and sizes).  ``forward`` is the tensor-level
+convenience that allocates ``o``, ``lse`` and any split-K/V workspace with
+torch and calls ``fa2_fwd_ex`` on the current stream.
 """
 from __future__ import annotations
 
@@ -17,8 +18,9 @@ import math
 import os
 
 __all__ = ["FA2_DTYPE_F32", "FA2_DTYPE_BF16", "FA2_OK", "FA2_ERR_INVALID_ARGUMENT",
-           "FA2_ERR_UNSUPPORTED", "FA2_ERR_LAUNCH", "FA2_ERR_NO_DEVICE", "Fa2Error",
-           "fa2_fwd", "fa2_status_string", "forward", "library_path", "EXPORTED_SYMBOLS"]
+           "FA2_ERR_UNSUPPORTED", "FA2_ERR_LAUNCH", "FA2_ERR_NO_DEVICE", "FA2_MAX_SPLITS", "Fa2Error",
+           "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_workspace_bytes", "fa2_fwd_num_splits",
+           "fa2_status_string", "forward", "library_path", "EXPORTED_SYMBOLS"]
 
 FA2_DTYPE_F32 = 0
 FA2_DTYPE_BF16 = 1
@@ -29,7 +31,10 @@ FA2_ERR_UNSUPPORTED = 2
 FA2_ERR_LAUNCH = 3
 FA2_ERR_NO_DEVICE = 4
 
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_status_string")
+FA2_MAX_SPLITS = 128
+
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_ex", "fa2_fwd_num_splits", "fa2_fwd_workspace_bytes",
+                    "fa2_status_string")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa2.so")
@@ -74,6 +79,17 @@ def _load():
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
     ]
+    lib.fa2_fwd_ex.restype = ctypes.c_int
+    lib.fa2_fwd_ex.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+    ]
+    lib.fa2_fwd_workspace_bytes.restype = ctypes.c_int64
+    lib.fa2_fwd_workspace_bytes.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
+    lib.fa2_fwd_num_splits.restype = ctypes.c_int
+    lib.fa2_fwd_num_splits.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int, ctypes.c_int]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -95,6 +111,23 @@ def fa2_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, M: int, N:
     return int(_lib.fa2_fwd(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream))
 
 
+def fa2_fwd_ex(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Hk: int, M: int, N: int,
+               D: int, scale: float, causal: int, dtype: int, n_splits: int, workspace: int | None,
+               workspace_size: int, stream: int | None) -> int:
+    """Direct call of the extended C entry point (grouped-query heads, split
+    K/V); pointers are integers.  Returns the fa2_status code."""
+    return int(_lib.fa2_fwd_ex(q, k, v, o, lse, B, H, Hk, M, N, D, scale, causal, dtype, n_splits,
+                               workspace, workspace_size, stream))
+
+
+def fa2_fwd_workspace_bytes(B: int, H: int, M: int, D: int, n_splits: int) -> int:
+    return int(_lib.fa2_fwd_workspace_bytes(B, H, M, D, n_splits))
+
+
+def fa2_fwd_num_splits(B: int, H: int, M: int, N: int, D: int, causal: int, dtype: int) -> int:
+    return int(_lib.fa2_fwd_num_splits(B, H, M, N, D, causal, dtype))
+
+
 def fa2_status_string(status: int) -> str:
     return _lib.fa2_status_string(int(status)).decode()
 
@@ -108,12 +141,17 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
 
 
-def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            n_splits: int = 1, workspace=None):
     """Attention forward on the current CUDA/HIP stream.
 
-    q: [B,H,M,D], k/v: [B,H,N,D] contiguous device tensors of one dtype
-    (float32 or bfloat16).  Returns (o [B,H,M,D] in q's dtype, lse [B,H,M]
-    float32).  ``scale`` defaults to 1/sqrt(D).
+    q: [B,H,M,D], k/v: [B,Hk,N,D] contiguous device tensors of one dtype
+    (float32 or bfloat16), H % Hk == 0 (query head h reads K/V head
+    h // (H // Hk)).  Returns (o [B,H,M,D] in q's dtype, lse [B,H,M]
+    float32).  ``scale`` defaults to 1/sqrt(D).  ``n_splits``: 1 = one kernel
+    over all keys, 0 = library's choice, >1 = split K/V with a combine kernel;
+    the workspace it needs is allocated with torch unless ``workspace`` (a
+    device tensor of at least ``fa2_fwd_workspace_bytes`` bytes) is given.
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -124,8 +162,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
     B, H, M, D = q.shape
-    N = k.shape[2]
-    if k.shape != (B, H, N, D) or v.shape != (B, H, N, D):
+    Hk, N = k.shape[1], k.shape[2]
+    if k.shape != (B, Hk, N, D) or v.shape != (B, Hk, N, D) or Hk < 1 or H % Hk:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -137,10 +175,21 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
     elif lse.shape != (B, H, M) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor of shape [B,H,M]")
+    code = _dtype_code(q)
+    splits = fa2_fwd_num_splits(B, H, M, N, D, int(bool(causal)), code) if n_splits == 0 else int(n_splits)
+    ws_ptr, ws_size = None, 0
+    if splits > 1:
+        need = fa2_fwd_workspace_bytes(B, H, M, D, splits)
+        if need < 0:
+            raise ValueError(f"invalid split count {splits}")
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_size = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        st = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                     B, H, M, N, D, float(scale), int(bool(causal)), _dtype_code(q), stream)
+        st = fa2_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, Hk, M, N, D, float(scale), int(bool(causal)), code, splits,
+                        ws_ptr, ws_size, stream)
     if st != FA2_OK:
         raise Fa2Error(st)
     return out, lse

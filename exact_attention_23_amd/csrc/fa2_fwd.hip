@@ -56,6 +56,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "fa2.h"
 
 namespace {
@@ -67,6 +69,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 
 // Buffer resource over `bytes` bytes at `base` (raw, no stride, dword data
 // format): loads past the end return zero instead of touching memory.
@@ -135,6 +138,82 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------
+// parameters and work assignment shared by the forward kernels
+// ---------------------------------------------------------------------------
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    float* ws_o;          // split K/V: partial O [n_splits, BH, M, D] fp32, else null
+    float* ws_l;          // split K/V: partial L [n_splits, BH, M] fp32, else null
+    int BH;               // batch * query heads
+    int H;                // query heads
+    int G;                // query heads per K/V head (H / Hk)
+    int M, N;
+    int n_qt;             // query tiles per head
+    int tiles_per_split;  // K/V tiles per split (at least all of them when unsplit)
+    float c_log2;         // scale * log2(e)
+};
+
+// One workgroup's task: query tile qt of head bh, reading K/V head bkv
+// (query head h uses K/V head h / G, "From FlashAttention to FlashAttention 2",
+// section "Layer 8"), over K/V tiles [t_begin, t_begin + n_kv) of its split.
+struct WgTask {
+    int bh, bkv, qt, split;
+    int t_begin;    // first K/V tile of the split
+    int n_kv;       // K/V tiles of this workgroup (0 for a split past the diagonal)
+    int n_kv_full;  // K/V tiles the query tile needs when unsplit
+};
+
+// Grid order: split-major, then query tile (heaviest first when causal), then
+// batch*head fastest, so that the tiles of one head spread over the XCDs in
+// step and every XCD gets the same mix of heavy and light tiles.
+template <bool CAUSAL, bool SPLIT>
+__device__ __forceinline__ WgTask wg_task(const FwdParams& p, int BM, int BN) {
+    WgTask t;
+    const int wg = blockIdx.x;
+    int r = wg;
+    t.split = 0;
+    if (SPLIT) {
+        const int per_split = p.BH * p.n_qt;
+        t.split = wg / per_split;
+        r = wg - t.split * per_split;
+    }
+    t.bh = r % p.BH;
+    t.qt = r / p.BH;
+    if (CAUSAL) t.qt = p.n_qt - 1 - t.qt;
+    // bh = (b * Hk + hk) * G + g for query head h = hk * G + g
+    t.bkv = p.G == 1 ? t.bh : t.bh / p.G;
+    const int kv_end = CAUSAL ? min(p.N, t.qt * BM + BM) : p.N;
+    t.n_kv_full = (kv_end + BN - 1) / BN;
+    t.t_begin = t.split * p.tiles_per_split;
+    t.n_kv = max(0, min(t.n_kv_full - t.t_begin, p.tiles_per_split));
+    return t;
+}
+
+// K/V tiles (of the workgroup's range) that a wave whose rows start at qw0
+// needs: causal rows stop at their diagonal, rows past M need none.
+template <bool CAUSAL>
+__device__ __forceinline__ int wave_tiles(const FwdParams& p, const WgTask& t, int qw0, int rows, int BN) {
+    if (qw0 >= p.M) return 0;
+    int n = t.n_kv_full;
+    if (CAUSAL) n = min(n, (min(p.N, qw0 + rows) + BN - 1) / BN);
+    return max(0, min(n - t.t_begin, t.n_kv));
+}
+
+// Split-K/V partial result of one query row (the lane's 4 consecutive O values
+// at d): O normalised by the split's own sum, and the split's L (-inf when the
+// split saw no visible key; its O is then 0).
+__device__ __forceinline__ float* partial_row(const FwdParams& p, const WgTask& t, int query, int D) {
+    return p.ws_o + (((int64_t)t.split * p.BH + t.bh) * p.M + query) * D;
+}
+__device__ __forceinline__ float* partial_l(const FwdParams& p, const WgTask& t, int query) {
+    return p.ws_l + ((int64_t)t.split * p.BH + t.bh) * p.M + query;
+}
+
+// ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
 // D: head dim (64 or 128); BN: keys per K/V tile (multiple of 32);
@@ -189,13 +268,17 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 __device__ constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-template <int D, int BN, int NW, int QB, int WAVES_PER_SIMD, bool CAUSAL>
+template <int D, int BN, int NW, int QB, int WAVES_PER_SIMD, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64, WAVES_PER_SIMD)
-fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                    const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                    float* __restrict__ LSE, int BH, int M, int N, int n_qt,
-                    float c_log2) {
+fa2_fwd_bf16_kernel(const FwdParams p) {
     using T = Bf16Traits<D, BN, NW, QB>;
+    const __bf16* __restrict__ Q = static_cast<const __bf16*>(p.q);
+    const __bf16* __restrict__ K = static_cast<const __bf16*>(p.k);
+    const __bf16* __restrict__ V = static_cast<const __bf16*>(p.v);
+    __bf16* __restrict__ O = static_cast<__bf16*>(p.o);
+    float* __restrict__ LSE = p.lse;
+    const int M = p.M, N = p.N;
+    const float c_log2 = p.c_log2;
     // Two K/V tile buffers, each BN rows x D bf16 (rows unpadded, chunks
     // swizzled).  They are separate arrays, and the loop below is unrolled by
     // two so every access names its buffer statically: the compiler can then
@@ -212,23 +295,18 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
-    // workgroup -> (batch*head, query tile); causal: heaviest tiles first
-    const int wg = blockIdx.x;
-    const int bh = wg % BH;
-    int qt = wg / BH;
-    if (CAUSAL) qt = n_qt - 1 - qt;
-    const int q0 = qt * T::kBM;
-    const int qw0 = q0 + wave * T::kQPW;  // first query row of this wave
+    const WgTask task = wg_task<CAUSAL, SPLIT>(p, T::kBM, BN);
+    const int bh = task.bh;
+    const int qw0 = task.qt * T::kBM + wave * T::kQPW;  // first query row of this wave
 
     const __bf16* Qh = Q + (int64_t)bh * M * D;
-    const __bf16* Kh = K + (int64_t)bh * N * D;
-    const __bf16* Vh = V + (int64_t)bh * N * D;
+    const __bf16* Kh = K + (int64_t)task.bkv * N * D;
+    const __bf16* Vh = V + (int64_t)task.bkv * N * D;
 
-    const int kv_end = CAUSAL ? min(N, q0 + T::kBM) : N;
-    const int n_kv = (kv_end + BN - 1) / BN;
-    int n_kv_wave = n_kv;
-    if (CAUSAL) n_kv_wave = min(n_kv, (min(N, qw0 + T::kQPW) + BN - 1) / BN);
-    if (qw0 >= M) n_kv_wave = 0;  // the wave holds only rows past M
+    // local tile kt is K/V tile kv_t0 + kt of the head
+    const int kv_t0 = task.t_begin;
+    const int n_kv = task.n_kv;
+    const int n_kv_wave = wave_tiles<CAUSAL>(p, task, qw0, T::kQPW, BN);
 
     // ---- Q fragments: B operand of S^T = K Q^T (lane = query, 8 d values)
     bf16x8 qf[QB][T::kDS];
@@ -273,8 +351,8 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         cp_voff[i] = (uint32_t)(r * T::kRowBytes + 16 * (p ^ swz_v<D>(r)));
     }
     auto issue_tile = [&](int kt, char* kdst, char* vdst) {
-        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Kh, cp_koff, wave_u, kt, N, kdst);
-        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Vh, cp_voff, wave_u, kt, N, vdst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Kh, cp_koff, wave_u, kv_t0 + kt, N, kdst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Vh, cp_voff, wave_u, kv_t0 + kt, N, vdst);
     };
 
     // per-lane parts of the LDS fragment addresses
@@ -295,6 +373,7 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         v_lane_off[db] = v_row_lane * T::kRowBytes + 16 * (c ^ swz_v<D>(v_row_lane)) + 8 * (va & 1);
     }
 
+    // kt: K/V tile of the head (only the mask uses it)
     auto compute_tile = [&](auto mask_tag, int kt, const char* klds, const char* vlds) {
         constexpr bool MASK = decltype(mask_tag)::value;
         // S^T = K Q^T for BN keys x QPW queries; K fragments are read one
@@ -436,11 +515,11 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // wave's first query row; all other tiles take the mask-free path.
     auto run_tile = [&](int kt, const char* klds, const char* vlds) {
         if (kt >= n_kv_wave) return;
-        const int kbase = kt * BN;
+        const int kbase = (kv_t0 + kt) * BN;
         if (kbase + BN > N || (CAUSAL && kbase + BN - 1 > qw0))
-            compute_tile(std::true_type{}, kt, klds, vlds);
+            compute_tile(std::true_type{}, kv_t0 + kt, klds, vlds);
         else
-            compute_tile(std::false_type{}, kt, klds, vlds);
+            compute_tile(std::false_type{}, kv_t0 + kt, klds, vlds);
     };
     for (int kt = 0; kt < n_kv; kt += 2) {
         if (kt + 1 < n_kv) issue_tile(kt + 1, sK1, sV1);
@@ -464,18 +543,32 @@ fa2_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         const int query = qw0 + 32 * qb + l32;
         if (query < M) {
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            __bf16* orow = O + ((int64_t)bh * M + query) * D;
+            const float lse = (m_run[qb] + fast_log2(l_ex)) * kLn2;
+            if constexpr (SPLIT) {
+                float* orow = partial_row(p, task, query, D);
 #pragma unroll
-            for (int db = 0; db < T::kDB; ++db)
+                for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d = 32 * db + 8 * g + 4 * h;
-                    uint32_t w[2];
-                    w[0] = pack_bf16x2(oacc[db][qb][4 * g + 0] * inv, oacc[db][qb][4 * g + 1] * inv);
-                    w[1] = pack_bf16x2(oacc[db][qb][4 * g + 2] * inv, oacc[db][qb][4 * g + 3] * inv);
-                    *reinterpret_cast<uint2*>(orow + d) = make_uint2(w[0], w[1]);
-                }
-            if (h == 0) LSE[(int64_t)bh * M + query] = (m_run[qb] + fast_log2(l_ex)) * kLn2;
+                    for (int g = 0; g < 4; ++g) {
+                        const floatx4 x = {oacc[db][qb][4 * g + 0] * inv, oacc[db][qb][4 * g + 1] * inv,
+                                           oacc[db][qb][4 * g + 2] * inv, oacc[db][qb][4 * g + 3] * inv};
+                        *reinterpret_cast<floatx4*>(orow + 32 * db + 8 * g + 4 * h) = x;
+                    }
+                if (h == 0) *partial_l(p, task, query) = lse;
+            } else {
+                __bf16* orow = O + ((int64_t)bh * M + query) * D;
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int d = 32 * db + 8 * g + 4 * h;
+                        uint32_t w[2];
+                        w[0] = pack_bf16x2(oacc[db][qb][4 * g + 0] * inv, oacc[db][qb][4 * g + 1] * inv);
+                        w[1] = pack_bf16x2(oacc[db][qb][4 * g + 2] * inv, oacc[db][qb][4 * g + 3] * inv);
+                        *reinterpret_cast<uint2*>(orow + d) = make_uint2(w[0], w[1]);
+                    }
+                if (h == 0) LSE[(int64_t)bh * M + query] = lse;
+            }
         }
     }
 }
@@ -525,13 +618,17 @@ struct PPTraits {
     static_assert(kTileChunks % (64 * kNW) == 0, "loader split");
 };
 
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(512, 2)
-fa2_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                       const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                       float* __restrict__ LSE, int BH, int M, int N, int n_qt,
-                       float c_log2) {
+fa2_fwd_bf16_pp_kernel(const FwdParams p) {
     using T = PPTraits<D, BN>;
+    const __bf16* __restrict__ Q = static_cast<const __bf16*>(p.q);
+    const __bf16* __restrict__ K = static_cast<const __bf16*>(p.k);
+    const __bf16* __restrict__ V = static_cast<const __bf16*>(p.v);
+    __bf16* __restrict__ O = static_cast<__bf16*>(p.o);
+    float* __restrict__ LSE = p.lse;
+    const int M = p.M, N = p.N;
+    const float c_log2 = p.c_log2;
     __shared__ __attribute__((aligned(1024))) char sK0[T::kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV0[T::kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sK1[T::kTileBytes];
@@ -544,23 +641,18 @@ fa2_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
-    // workgroup -> (batch*head, query tile); causal: heaviest tiles first
-    const int wg = blockIdx.x;
-    const int bh = wg % BH;
-    int qt = wg / BH;
-    if (CAUSAL) qt = n_qt - 1 - qt;
-    const int q0 = qt * T::kBM;
-    const int qw0 = q0 + 32 * (2 * (wave & 3) + grp);  // first query row of this wave
+    const WgTask task = wg_task<CAUSAL, SPLIT>(p, T::kBM, BN);
+    const int bh = task.bh;
+    const int qw0 = task.qt * T::kBM + 32 * (2 * (wave & 3) + grp);  // first query row of this wave
 
     const __bf16* Qh = Q + (int64_t)bh * M * D;
-    const __bf16* Kh = K + (int64_t)bh * N * D;
-    const __bf16* Vh = V + (int64_t)bh * N * D;
+    const __bf16* Kh = K + (int64_t)task.bkv * N * D;
+    const __bf16* Vh = V + (int64_t)task.bkv * N * D;
 
-    const int kv_end = CAUSAL ? min(N, q0 + T::kBM) : N;
-    const int n_kv = (kv_end + BN - 1) / BN;
-    int n_w = n_kv;  // tiles this wave needs
-    if (CAUSAL) n_w = min(n_kv, (min(N, qw0 + 32) + BN - 1) / BN);
-    if (qw0 >= M) n_w = 0;
+    // local tile t is K/V tile kv_t0 + t of the head
+    const int kv_t0 = task.t_begin;
+    const int n_kv = task.n_kv;
+    const int n_w = wave_tiles<CAUSAL>(p, task, qw0, 32, BN);  // tiles this wave needs
 
     // ---- Q fragments: B operand of S^T = K Q^T (lane = query, 8 d values)
     bf16x8 qf[T::kDS];
@@ -595,7 +687,7 @@ fa2_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
         cp_voff[i] = (uint32_t)(r * T::kRowBytes + 16 * (p ^ swz_v<D>(r)));
     }
     auto issue_copy = [&](const __bf16* head, const uint32_t* cp_off, int kt, char* dst) {
-        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(head, cp_off, wave_u, kt, N, dst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(head, cp_off, wave_u, kv_t0 + kt, N, dst);
     };
 
     // ---- per-lane parts of the LDS fragment addresses
@@ -672,7 +764,7 @@ fa2_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
     // weights for L.
     auto valu_phase = [&](int t) {
         if (t < 0 || t >= n_w) return;
-        const int kbase = t * BN;
+        const int kbase = (kv_t0 + t) * BN;
         if (kbase + BN > N || (CAUSAL && kbase + BN - 1 > qw0)) {
             __asm__ volatile("");  // keep this a branch, not a select per element
             int lim = N - 1 - kbase;
@@ -778,17 +870,31 @@ fa2_fwd_bf16_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
         const int query = qw0 + l32;
         if (query < M) {
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            __bf16* orow = O + ((int64_t)bh * M + query) * D;
+            const float lse = (m_run + fast_log2(l_ex)) * kLn2;
+            if constexpr (SPLIT) {
+                float* orow = partial_row(p, task, query, D);
 #pragma unroll
-            for (int db = 0; db < T::kDB; ++db)
+                for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d = 32 * db + 8 * g + 4 * h;
-                    const uint32_t w0 = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-                    const uint32_t w1 = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-                    *reinterpret_cast<uint2*>(orow + d) = make_uint2(w0, w1);
-                }
-            if (h == 0) LSE[(int64_t)bh * M + query] = (m_run + fast_log2(l_ex)) * kLn2;
+                    for (int g = 0; g < 4; ++g) {
+                        const floatx4 x = {oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv,
+                                           oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
+                        *reinterpret_cast<floatx4*>(orow + 32 * db + 8 * g + 4 * h) = x;
+                    }
+                if (h == 0) *partial_l(p, task, query) = lse;
+            } else {
+                __bf16* orow = O + ((int64_t)bh * M + query) * D;
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int d = 32 * db + 8 * g + 4 * h;
+                        const uint32_t w0 = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+                        const uint32_t w1 = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+                        *reinterpret_cast<uint2*>(orow + d) = make_uint2(w0, w1);
+                    }
+                if (h == 0) LSE[(int64_t)bh * M + query] = lse;
+            }
         }
     }
 }
@@ -814,13 +920,17 @@ struct F32Traits {
     static constexpr size_t kLdsBytes = 2 * (kKElems + kVElems) * sizeof(float);
 };
 
-template <int D, int BN, int NW, bool CAUSAL>
+template <int D, int BN, int NW, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64)
-fa2_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
-                   const float* __restrict__ V, float* __restrict__ O,
-                   float* __restrict__ LSE, int BH, int M, int N, int n_qt,
-                   float c_log2) {
+fa2_fwd_f32_kernel(const FwdParams p) {
     using T = F32Traits<D, BN, NW>;
+    const float* __restrict__ Q = static_cast<const float*>(p.q);
+    const float* __restrict__ K = static_cast<const float*>(p.k);
+    const float* __restrict__ V = static_cast<const float*>(p.v);
+    float* __restrict__ O = static_cast<float*>(p.o);
+    float* __restrict__ LSE = p.lse;
+    const int M = p.M, N = p.N;
+    const float c_log2 = p.c_log2;
     __shared__ __attribute__((aligned(16))) float sK[2][T::kKElems];
     __shared__ __attribute__((aligned(16))) float sV[2][T::kVElems];
 
@@ -830,22 +940,18 @@ fa2_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
-    const int wg = blockIdx.x;
-    const int bh = wg % BH;
-    int qt = wg / BH;
-    if (CAUSAL) qt = n_qt - 1 - qt;
-    const int q0 = qt * T::kBM;
-    const int qw0 = q0 + wave * 32;
+    const WgTask task = wg_task<CAUSAL, SPLIT>(p, T::kBM, BN);
+    const int bh = task.bh;
+    const int qw0 = task.qt * T::kBM + wave * 32;
 
     const float* Qh = Q + (int64_t)bh * M * D;
-    const float* Kh = K + (int64_t)bh * N * D;
-    const float* Vh = V + (int64_t)bh * N * D;
+    const float* Kh = K + (int64_t)task.bkv * N * D;
+    const float* Vh = V + (int64_t)task.bkv * N * D;
 
-    const int kv_end = CAUSAL ? min(N, q0 + T::kBM) : N;
-    const int n_kv = (kv_end + BN - 1) / BN;
-    int n_kv_wave = n_kv;
-    if (CAUSAL) n_kv_wave = min(n_kv, (min(N, qw0 + 32) + BN - 1) / BN);
-    if (qw0 >= M) n_kv_wave = 0;
+    // local tile kt is K/V tile kv_t0 + kt of the head
+    const int kv_t0 = task.t_begin;
+    const int n_kv = task.n_kv;
+    const int n_kv_wave = wave_tiles<CAUSAL>(p, task, qw0, 32, BN);
 
     // Q: lane half h holds d in [h*D/2, (h+1)*D/2) of its query row; MFMA step s
     // contracts d = h*D/2 + s in both operands.
@@ -867,7 +973,7 @@ fa2_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
     u32x4 kreg[T::kPerThread], vreg[T::kPerThread];
     auto load_tile = [&](int kt) {
-        const int kbase = kt * BN;
+        const int kbase = (kv_t0 + kt) * BN;
 #pragma unroll
         for (int i = 0; i < T::kPerThread; ++i) {
             const int id = tid + i * T::kThreads;
@@ -920,7 +1026,7 @@ fa2_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                 }
             }
 
-            const int kbase = kt * BN;
+            const int kbase = (kv_t0 + kt) * BN;
             const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > qw0);
             if (need_mask) {
                 const int query = qw0 + l32;
@@ -977,7 +1083,9 @@ fa2_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int query = qw0 + l32;
     if (query < M) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float* orow = O + ((int64_t)bh * M + query) * D;
+        // split K/V: the partial result goes to the workspace (also fp32)
+        float* orow = SPLIT ? partial_row(p, task, query, D) : O + ((int64_t)bh * M + query) * D;
+        float* lrow = SPLIT ? partial_l(p, task, query) : LSE + (int64_t)bh * M + query;
 #pragma unroll
         for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
@@ -990,93 +1098,106 @@ fa2_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                 x[3] = oacc[db][4 * g + 3] * inv;
                 *reinterpret_cast<floatx4*>(orow + d) = x;
             }
-        if (h == 0) LSE[(int64_t)bh * M + query] = (m_run + fast_log2(l_tot)) * kLn2;
+        if (h == 0) *lrow = (m_run + fast_log2(l_tot)) * kLn2;
     }
+}
+
+// ---------------------------------------------------------------------------
+// split K/V: combine the partial results
+// ---------------------------------------------------------------------------
+// Split s saw the keys of its range only and stored O_s = sum_j e_j v_j / l_s
+// and L_s = log l_s with l_s = sum_j e_j, e_j = exp(score_j) over its visible
+// keys.  The full row has l = sum_s l_s, so L = log sum_s exp(L_s) and
+// O = sum_s exp(L_s - L) O_s exactly: the stored logsumexp is what makes the
+// partials combinable ("FlashAttention-2 from PyTorch to Triton", the role of
+// L; "From FlashAttention to FlashAttention 2", section "Layer 2", the
+// split-K/V path of the dispatch).
+// One wave per query row; each lane holds D / 64 consecutive values.
+template <typename OutT, int D>
+__global__ void __launch_bounds__(256)
+fa2_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_l, OutT* __restrict__ O,
+                 float* __restrict__ LSE, int rows, int n_splits) {
+    constexpr int kPer = D / 64;
+    static_assert(kPer == 1 || kPer == 2, "head dim");
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    float m = -INFINITY;
+    for (int s = 0; s < n_splits; ++s) m = fmaxf(m, ws_l[(int64_t)s * rows + row]);
+    float acc[kPer] = {};
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+        for (int s = 0; s < n_splits; ++s) {
+            const float w = fast_exp2((ws_l[(int64_t)s * rows + row] - m) * kLog2e);
+            if (w == 0.f) continue;  // a split that saw no visible key (L_s = -inf)
+            wsum += w;
+            const float* src = ws_o + ((int64_t)s * rows + row) * D + lane * kPer;
+            if constexpr (kPer == 2) {
+                const float2 x = *reinterpret_cast<const float2*>(src);
+                acc[0] = fmaf(w, x.x, acc[0]);
+                acc[1] = fmaf(w, x.y, acc[1]);
+            } else {
+                acc[0] = fmaf(w, src[0], acc[0]);
+            }
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    OutT* dst = O + (int64_t)row * D + lane * kPer;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) dst[i] = static_cast<OutT>(acc[i] * inv);  // bf16: nearest even
+    if (lane == 0) LSE[row] = m == -INFINITY ? -INFINITY : m + fast_log2(wsum) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
 // host side: validation, dispatch table, launch
 // ---------------------------------------------------------------------------
-struct LaunchArgs {
-    const void* q;
-    const void* k;
-    const void* v;
-    void* o;
-    float* lse;
-    int BH, M, N;
-    float c_log2;
-};
-
-typedef hipError_t (*launch_fn)(const LaunchArgs&, hipStream_t);
-
-template <int D, int BN, int NW, int QB, int WPS, bool CAUSAL>
-hipError_t launch_bf16(const LaunchArgs& a, hipStream_t stream) {
-    using T = Bf16Traits<D, BN, NW, QB>;
-    const int n_qt = (a.M + T::kBM - 1) / T::kBM;
-    const __bf16* q = static_cast<const __bf16*>(a.q);
-    const __bf16* k = static_cast<const __bf16*>(a.k);
-    const __bf16* v = static_cast<const __bf16*>(a.v);
-    __bf16* o = static_cast<__bf16*>(a.o);
-    float* lse = a.lse;
-    int BH = a.BH, M = a.M, N = a.N;
-    float c = a.c_log2;
-    void* args[] = {&q, &k, &v, &o, &lse, &BH, &M, &N, (void*)&n_qt, &c};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fa2_fwd_bf16_kernel<D, BN, NW, QB, WPS, CAUSAL>),
-                           dim3((unsigned)(n_qt * a.BH)), dim3(T::kThreads), args, 0, stream);
-}
-
-template <int D, int BN, bool CAUSAL>
-hipError_t launch_bf16_pp(const LaunchArgs& a, hipStream_t stream) {
-    using T = PPTraits<D, BN>;
-    const int n_qt = (a.M + T::kBM - 1) / T::kBM;
-    const __bf16* q = static_cast<const __bf16*>(a.q);
-    const __bf16* k = static_cast<const __bf16*>(a.k);
-    const __bf16* v = static_cast<const __bf16*>(a.v);
-    __bf16* o = static_cast<__bf16*>(a.o);
-    float* lse = a.lse;
-    int BH = a.BH, M = a.M, N = a.N;
-    float c = a.c_log2;
-    void* args[] = {&q, &k, &v, &o, &lse, &BH, &M, &N, (void*)&n_qt, &c};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fa2_fwd_bf16_pp_kernel<D, BN, CAUSAL>),
-                           dim3((unsigned)(n_qt * a.BH)), dim3(T::kThreads), args, 0, stream);
-}
-
-template <int D, int BN, int NW, bool CAUSAL>
-hipError_t launch_f32(const LaunchArgs& a, hipStream_t stream) {
-    using T = F32Traits<D, BN, NW>;
-    const int n_qt = (a.M + T::kBM - 1) / T::kBM;
-    const float* q = static_cast<const float*>(a.q);
-    const float* k = static_cast<const float*>(a.k);
-    const float* v = static_cast<const float*>(a.v);
-    float* o = static_cast<float*>(a.o);
-    float* lse = a.lse;
-    int BH = a.BH, M = a.M, N = a.N;
-    float c = a.c_log2;
-    void* args[] = {&q, &k, &v, &o, &lse, &BH, &M, &N, (void*)&n_qt, &c};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fa2_fwd_f32_kernel<D, BN, NW, CAUSAL>),
-                           dim3((unsigned)(n_qt * a.BH)), dim3(T::kThreads), args, 0, stream);
-}
-
 // Dispatch on (dtype, head dim, causal), as the pages' C++ entry point does
 // with its dtype/head-dim/bool switches; each entry is one compiled kernel.
 struct Entry {
     int dtype, D, causal;
-    launch_fn fn;
-    int block_m;
+    const void* kernel;        // whole key range, writes o and lse
+    const void* kernel_split;  // one key range per split, writes the workspace
+    int threads;
+    int block_m;    // query rows per workgroup
+    int block_n;    // keys per K/V tile
+    int wg_per_cu;  // workgroups resident per CU (registers / LDS)
 };
 
+#define FWD_KERNEL(...) reinterpret_cast<const void*>(&__VA_ARGS__)
+#define FWD_PAIR(name, ...) FWD_KERNEL(name<__VA_ARGS__, false>), FWD_KERNEL(name<__VA_ARGS__, true>)
 const Entry kTable[] = {
     // bf16: 8 waves (two per SIMD) share each K/V tile; 256 query rows per
     // workgroup; 64-key tiles at D=128, 128-key tiles at D=64 (measured best)
-    {FA2_DTYPE_BF16, 64, 0, &launch_bf16<64, 128, 8, 1, 2, false>, 256},
-    {FA2_DTYPE_BF16, 64, 1, &launch_bf16<64, 128, 8, 1, 2, true>, 256},
-    {FA2_DTYPE_BF16, 128, 0, &launch_bf16_pp<128, 64, false>, 256},
-    {FA2_DTYPE_BF16, 128, 1, &launch_bf16_pp<128, 64, true>, 256},
-    {FA2_DTYPE_F32, 64, 0, &launch_f32<64, 64, 4, false>, 128},
-    {FA2_DTYPE_F32, 64, 1, &launch_f32<64, 64, 4, true>, 128},
-    {FA2_DTYPE_F32, 128, 0, &launch_f32<128, 32, 4, false>, 128},
-    {FA2_DTYPE_F32, 128, 1, &launch_f32<128, 32, 4, true>, 128},
+    {FA2_DTYPE_BF16, 64, 0, FWD_PAIR(fa2_fwd_bf16_kernel, 64, 128, 8, 1, 2, false), 512, 256, 128, 1},
+    {FA2_DTYPE_BF16, 64, 1, FWD_PAIR(fa2_fwd_bf16_kernel, 64, 128, 8, 1, 2, true), 512, 256, 128, 1},
+    {FA2_DTYPE_BF16, 128, 0, FWD_PAIR(fa2_fwd_bf16_pp_kernel, 128, 64, false), 512, 256, 64, 1},
+    {FA2_DTYPE_BF16, 128, 1, FWD_PAIR(fa2_fwd_bf16_pp_kernel, 128, 64, true), 512, 256, 64, 1},
+    {FA2_DTYPE_F32, 64, 0, FWD_PAIR(fa2_fwd_f32_kernel, 64, 64, 4, false), 256, 128, 64, 2},
+    {FA2_DTYPE_F32, 64, 1, FWD_PAIR(fa2_fwd_f32_kernel, 64, 64, 4, true), 256, 128, 64, 2},
+    {FA2_DTYPE_F32, 128, 0, FWD_PAIR(fa2_fwd_f32_kernel, 128, 32, 4, false), 256, 128, 32, 1},
+    {FA2_DTYPE_F32, 128, 1, FWD_PAIR(fa2_fwd_f32_kernel, 128, 32, 4, true), 256, 128, 32, 1},
 };
+#undef FWD_PAIR
+
+struct MergeEntry {
+    int dtype, D;
+    const void* kernel;
+};
+const MergeEntry kMergeTable[] = {
+    {FA2_DTYPE_BF16, 64, FWD_KERNEL(fa2_merge_kernel<__bf16, 64>)},
+    {FA2_DTYPE_BF16, 128, FWD_KERNEL(fa2_merge_kernel<__bf16, 128>)},
+    {FA2_DTYPE_F32, 64, FWD_KERNEL(fa2_merge_kernel<float, 64>)},
+    {FA2_DTYPE_F32, 128, FWD_KERNEL(fa2_merge_kernel<float, 128>)},
+};
+#undef FWD_KERNEL
+
+constexpr int kCUs = 256;  // MI355X; the split heuristic's design point
+
+const Entry* find_entry(int dtype, int64_t D, int causal) {
+    for (const Entry& t : kTable)
+        if (t.dtype == dtype && t.D == D && t.causal == causal) return &t;
+    return nullptr;
+}
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -1085,52 +1206,133 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split count that fills the GPU: 1 when the unsplit grid already occupies
+// three quarters of the workgroup slots; otherwise enough splits to fill them,
+// with at least two K/V tiles per split.
+int choose_splits(const Entry& e, int64_t BH, int64_t M, int64_t N) {
+    const int64_t base = BH * ceil_div(M, e.block_m);
+    const int64_t slots = (int64_t)kCUs * e.wg_per_cu;
+    if (base <= 0 || base * 4 >= slots * 3) return 1;
+    int64_t s = ceil_div(slots, base);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, ceil_div(N, e.block_n) / 2));
+    s = std::min<int64_t>(s, FA2_MAX_SPLITS);
+    return (int)std::max<int64_t>(1, s);
+}
+
+int64_t workspace_bytes(int64_t BH, int64_t M, int64_t D, int n_splits) {
+    if (n_splits <= 1) return 0;
+    const int64_t rows = (int64_t)n_splits * BH * M;
+    return ceil_div(rows * D * 4, 256) * 256 + rows * 4;
+}
+
 }  // namespace
 
-extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                       int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
-                       float scale, int causal, int dtype, void* stream) {
+extern "C" int64_t fa2_fwd_workspace_bytes(int64_t B, int64_t H, int64_t M, int64_t D, int n_splits) {
+    if (B < 0 || H < 0 || M < 0 || D <= 0 || n_splits < 1 || n_splits > FA2_MAX_SPLITS) return -1;
+    if (B > ((int64_t)1 << 31) || H > ((int64_t)1 << 31) || M > ((int64_t)1 << 31) || D > 4096) return -1;
+    return workspace_bytes(B * H, M, D, n_splits);
+}
+
+extern "C" int fa2_fwd_num_splits(int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, int causal, int dtype) {
+    if (B < 0 || H < 0 || M < 0 || N <= 0) return 1;
+    if (B > ((int64_t)1 << 31) || H > ((int64_t)1 << 31) || M > ((int64_t)1 << 31)) return 1;
+    const Entry* e = find_entry(dtype, D, causal);
+    if (!e) return 1;
+    return choose_splits(*e, B * H, M, N);
+}
+
+extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+                          float scale, int causal, int dtype, int n_splits,
+                          void* workspace, int64_t workspace_size, void* stream) {
     // ---- argument checks, all before any HIP call
     if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARGUMENT;
-    if (B < 0 || H < 0 || M < 0 || N <= 0 || D <= 0) return FA2_ERR_INVALID_ARGUMENT;
+    if (B < 0 || H < 0 || Hk < 1 || M < 0 || N <= 0 || D <= 0) return FA2_ERR_INVALID_ARGUMENT;
+    if (H > 0 && (Hk > H || H % Hk != 0)) return FA2_ERR_INVALID_ARGUMENT;
     if (dtype != FA2_DTYPE_F32 && dtype != FA2_DTYPE_BF16) return FA2_ERR_INVALID_ARGUMENT;
     if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARGUMENT;
     if (!(scale > 0.f) || !isfinite(scale)) return FA2_ERR_INVALID_ARGUMENT;
+    if (n_splits < 0 || n_splits > FA2_MAX_SPLITS) return FA2_ERR_INVALID_ARGUMENT;
+    if (workspace_size < 0) return FA2_ERR_INVALID_ARGUMENT;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
         misaligned(lse, 4))
         return FA2_ERR_INVALID_ARGUMENT;
 
-    const Entry* e = nullptr;
-    for (const Entry& t : kTable)
-        if (t.dtype == dtype && t.D == D && t.causal == causal) e = &t;
+    const Entry* e = find_entry(dtype, D, causal);
     if (!e) return FA2_ERR_UNSUPPORTED;
 
     // sizes: per-head offsets are 32-bit in the kernels, the grid is 1-D
     const int64_t kMax = (int64_t)1 << 31;
-    if (B > kMax || H > kMax) return FA2_ERR_UNSUPPORTED;
+    if (B > kMax || H > kMax || M >= kMax || N >= kMax) return FA2_ERR_UNSUPPORTED;
     const int64_t BH = B * H;
     if (M * D >= kMax || N * D >= kMax || BH >= kMax) return FA2_ERR_UNSUPPORTED;
-    const int64_t n_qt = (M + e->block_m - 1) / e->block_m;
-    if (n_qt * BH >= kMax) return FA2_ERR_UNSUPPORTED;
+    const int splits = n_splits == 0 ? choose_splits(*e, BH, M, N) : n_splits;
+    const int64_t n_qt = ceil_div(M, e->block_m);
+    if (n_qt * BH * splits >= kMax) return FA2_ERR_UNSUPPORTED;
 
     const size_t elt = dtype == FA2_DTYPE_F32 ? 4 : 2;
     const size_t o_bytes = (size_t)BH * M * D * elt;
-    const size_t kv_bytes = (size_t)BH * N * D * elt;
+    const size_t kv_bytes = (size_t)B * Hk * N * D * elt;
     const size_t lse_bytes = (size_t)BH * M * 4;
     if (overlaps(o, o_bytes, q, o_bytes) || overlaps(o, o_bytes, k, kv_bytes) ||
         overlaps(o, o_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, q, o_bytes) ||
         overlaps(lse, lse_bytes, k, kv_bytes) || overlaps(lse, lse_bytes, v, kv_bytes) ||
         overlaps(lse, lse_bytes, o, o_bytes))
         return FA2_ERR_INVALID_ARGUMENT;
+    const int64_t ws_need = workspace_bytes(BH, M, D, splits);
+    if (ws_need > 0) {
+        if (!workspace || workspace_size < ws_need || misaligned(workspace, 16))
+            return FA2_ERR_INVALID_ARGUMENT;
+        const size_t w = (size_t)ws_need;
+        if (overlaps(workspace, w, q, o_bytes) || overlaps(workspace, w, k, kv_bytes) ||
+            overlaps(workspace, w, v, kv_bytes) || overlaps(workspace, w, o, o_bytes) ||
+            overlaps(workspace, w, lse, lse_bytes))
+            return FA2_ERR_INVALID_ARGUMENT;
+    }
 
     if (M == 0 || BH == 0) return FA2_OK;
 
-    LaunchArgs a;
-    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.BH = (int)BH; a.M = (int)M; a.N = (int)N;
-    a.c_log2 = scale * 1.44269504088896340736f;  // scale * log2(e)
-    const hipError_t err = e->fn(a, static_cast<hipStream_t>(stream));
+    FwdParams prm;
+    prm.q = q; prm.k = k; prm.v = v; prm.o = o; prm.lse = lse;
+    prm.BH = (int)BH; prm.H = (int)H; prm.G = (int)(H / Hk);
+    prm.M = (int)M; prm.N = (int)N;
+    prm.n_qt = (int)n_qt;
+    prm.c_log2 = scale * 1.44269504088896340736f;  // scale * log2(e)
+    const int64_t n_tiles = ceil_div(N, e->block_n);
+    if (splits > 1) {
+        prm.ws_o = static_cast<float*>(workspace);
+        prm.ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + ceil_div(splits * BH * M * D * 4, 256) * 256);
+        prm.tiles_per_split = (int)ceil_div(n_tiles, splits);
+    } else {
+        prm.ws_o = prm.ws_l = nullptr;
+        prm.tiles_per_split = (int)n_tiles;
+    }
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void* args[] = {&prm};
+    hipError_t err = hipLaunchKernel(splits > 1 ? e->kernel_split : e->kernel, dim3((unsigned)(n_qt * BH * splits)),
+                                     dim3(e->threads), args, 0, st);
+    if (err == hipSuccess && splits > 1) {
+        const MergeEntry* me = nullptr;
+        for (const MergeEntry& t : kMergeTable)
+            if (t.dtype == dtype && t.D == D) me = &t;
+        if (!me) return FA2_ERR_UNSUPPORTED;  // unreachable: every forward entry has a merge
+        const float* ws_o = prm.ws_o;
+        const float* ws_l = prm.ws_l;
+        int rows = (int)(BH * M), ns = splits;
+        void* margs[] = {(void*)&ws_o, (void*)&ws_l, &o, &lse, &rows, &ns};
+        err = hipLaunchKernel(me->kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), margs, 0, st);
+    }
     return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+                       float scale, int causal, int dtype, void* stream) {
+    return fa2_fwd_ex(q, k, v, o, lse, B, H, H > 0 ? H : 1, M, N, D, scale, causal, dtype, 1, nullptr, 0,
+                      stream);
 }
 
 extern "C" const char* fa2_status_string(int status) {

@@ -94,6 +94,62 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
             float scale, int causal, int dtype, void* stream);
 
+/* Upper bound of the n_splits argument of fa2_fwd_ex. */
+#define FA2_MAX_SPLITS 128
+
+/*
+ * fa2_fwd_ex -- fa2_fwd with the other options of the pages' C++ entry point
+ * ("From FlashAttention to FlashAttention 2", section "Layer 2": dispatch on
+ * dtype, head dimension, causal and the number of K/V splits; section
+ * "Layer 8": grouped-query attention).
+ *
+ * Differences from fa2_fwd:
+ *   Hk        key/value heads, 1 <= Hk <= H with H % Hk == 0 (any Hk >= 1 when
+ *             H == 0).  k and v are [B, Hk, N, D]; query head h reads K/V head
+ *             h / (H / Hk).  Hk == H is multi-head attention (fa2_fwd),
+ *             Hk == 1 multi-query attention.
+ *   n_splits  0: the library chooses (fa2_fwd_num_splits); 1: one kernel over
+ *             the whole key range, no workspace; 2..FA2_MAX_SPLITS: the key
+ *             range [0, N) is cut into n_splits ranges of whole K/V tiles,
+ *             each processed by its own workgroups, which write a partial O
+ *             (fp32, normalised within the range) and the range's logsumexp;
+ *             a second kernel combines them, O = sum_s exp(L_s - L) O_s with
+ *             L = log sum_s exp(L_s).  Ranges past a causal row's diagonal
+ *             are empty and contribute nothing.  The result matches the
+ *             unsplit one to rounding (not bitwise); it is deterministic.
+ *   workspace, workspace_size
+ *             device memory the caller owns for the partial results when the
+ *             effective split count is > 1: at least
+ *             fa2_fwd_workspace_bytes(B, H, M, D, splits) bytes, 16-byte
+ *             aligned, overlapping no other buffer; its contents on entry do
+ *             not matter and on return are unspecified.  Ignored (may be NULL)
+ *             when the effective split count is 1.
+ * Both kernels are enqueued on `stream`; with splits the call returns after
+ * enqueueing the second.  Errors as for fa2_fwd; a missing or short
+ * workspace, or n_splits outside [0, FA2_MAX_SPLITS], is
+ * FA2_ERR_INVALID_ARGUMENT.
+ */
+int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+               int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+               float scale, int causal, int dtype, int n_splits,
+               void* workspace, int64_t workspace_size, void* stream);
+
+/*
+ * fa2_fwd_workspace_bytes -- workspace fa2_fwd_ex needs for n_splits splits
+ * (0 when n_splits == 1); -1 for invalid arguments (negative sizes, D <= 0,
+ * n_splits outside [1, FA2_MAX_SPLITS]).  Pure host computation.
+ */
+int64_t fa2_fwd_workspace_bytes(int64_t B, int64_t H, int64_t M, int64_t D, int n_splits);
+
+/*
+ * fa2_fwd_num_splits -- the split count fa2_fwd_ex uses for n_splits == 0:
+ * 1 when B * H * ceil(M / rows_per_workgroup) already fills about three
+ * quarters of the GPU's workgroup slots (256 CUs), else enough splits to fill
+ * them, keeping at least two K/V tiles per split.  Returns 1 for arguments
+ * fa2_fwd_ex would reject.  Pure host computation.
+ */
+int fa2_fwd_num_splits(int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, int causal, int dtype);
+
 /* Static, NUL-terminated description of a fa2_status value. */
 const char* fa2_status_string(int status);
 

@@ -45,6 +45,12 @@ def _bind(lib):
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
     ]
+    lib.fa2_oracle_fwd_gqa.restype = ctypes.c_int
+    lib.fa2_oracle_fwd_gqa.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+    ]
     lib.fa2_oracle_max_threads.restype = ctypes.c_int
     lib.fa2_oracle_max_threads.argtypes = []
     return lib
@@ -65,13 +71,13 @@ def max_threads() -> int:
 
 
 def _as_f32(x) -> np.ndarray:
-    """Exact float32 carrier of the input values (fp32 as is, bf16 widened)."""
+    """Exact float32 carrier of the input values (fp32 as is, bf16/fp16 widened)."""
     try:
         import torch
         if isinstance(x, torch.Tensor):
             x = x.detach().to("cpu")
-            if x.dtype not in (torch.float32, torch.bfloat16):
-                raise TypeError(f"oracle inputs must be float32 or bfloat16, got {x.dtype}")
+            if x.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+                raise TypeError(f"oracle inputs must be float32, bfloat16 or float16, got {x.dtype}")
             x = x.to(torch.float32).contiguous().numpy()
     except ImportError:  # pragma: no cover - torch is always present here
         pass
@@ -85,7 +91,8 @@ def attention(q, k, v, scale: float, causal: bool, rows: Optional[np.ndarray] = 
               threads: int = 0, _lib_override=None):
     """Reference attention forward.
 
-    q: [B,H,M,D], k/v: [B,H,N,D] (torch tensors or float32 numpy arrays).
+    q: [B,H,M,D], k/v: [B,Hk,N,D] with H % Hk == 0 (torch tensors or float32
+    numpy arrays); query head h reads K/V head h // (H // Hk).
     rows: optional int64 array of query rows (same for every head); when
     given, outputs cover only those rows.
     Returns (o, lse) as float64 numpy arrays: o [B,H,R,D], lse [B,H,R].
@@ -94,8 +101,8 @@ def attention(q, k, v, scale: float, causal: bool, rows: Optional[np.ndarray] = 
     if qa.ndim != 4 or ka.ndim != 4 or va.ndim != 4:
         raise ValueError("q, k, v must be 4-D [B,H,seq,D]")
     B, H, M, D = qa.shape
-    N = ka.shape[2]
-    if ka.shape != (B, H, N, D) or va.shape != (B, H, N, D):
+    Hk, N = ka.shape[1], ka.shape[2]
+    if ka.shape != (B, Hk, N, D) or va.shape != (B, Hk, N, D) or Hk < 1 or H % Hk:
         raise ValueError(f"shape mismatch q{qa.shape} k{ka.shape} v{va.shape}")
     if rows is not None:
         rows_a = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
@@ -108,9 +115,14 @@ def attention(q, k, v, scale: float, causal: bool, rows: Optional[np.ndarray] = 
     o = np.empty((B, H, R, D), dtype=np.float64)
     lse = np.empty((B, H, R), dtype=np.float64)
     lib = _load() if _lib_override is None else _lib_override
-    rc = lib.fa2_oracle_fwd(qa.ctypes.data, ka.ctypes.data, va.ctypes.data,
+    if Hk == H:
+        rc = lib.fa2_oracle_fwd(qa.ctypes.data, ka.ctypes.data, va.ctypes.data,
                                 o.ctypes.data, lse.ctypes.data, B, H, M, N, D,
                                 float(scale), int(bool(causal)), rows_p, R, int(threads))
+    else:
+        rc = lib.fa2_oracle_fwd_gqa(qa.ctypes.data, ka.ctypes.data, va.ctypes.data,
+                                    o.ctypes.data, lse.ctypes.data, B, H, Hk, M, N, D,
+                                    float(scale), int(bool(causal)), rows_p, R, int(threads))
     if rc != 0:
         raise ValueError(f"fa2_oracle_fwd failed with status {rc}")
     del rows_a

@@ -9,7 +9,7 @@
  * What it computes is the plain definition of scaled-dot-product attention,
  * evaluated one query row at a time in IEEE double precision:
  *
- *   for every (b, h) and query row i:
+ *   for every (b, h) and query row i, with K/V head hk = h / (H / Hk):
  *     J     = {0..N-1}, or {0..min(i, N-1)} when causal          (1)
  *     s_j   = scale * sum_d q[i,d] * k[j,d]          for j in J    (2)
  *     m     = max_{j in J} s_j                                     (3)
@@ -31,6 +31,10 @@
  *           m + log(l): "FlashAttention-2 from PyTorch to Triton", opening
  *           description of the second output L; "From FlashAttention to
  *           FlashAttention 2", section "Backward Pass: Recomputation".
+ *  (hk)     grouped-query attention: H / Hk consecutive query heads share one
+ *           K/V head ("From FlashAttention to FlashAttention 2", section
+ *           "Layer 8": the K/V head index is the query head index divided by
+ *           the ratio h / h_k).  Hk == H is ordinary multi-head attention.
  *  (3),(4)  subtracting the row maximum before exponentiating does not
  *           change (5) or (6) mathematically; it keeps exp() finite for the
  *           large-magnitude workloads.  The pages' harness uses
@@ -40,8 +44,8 @@
  * No blocking, fusion or reordering beyond the definition: one fp64 score
  * row per query, materialised, then exponentiated, then used.
  *
- * Inputs are float arrays: fp32 inputs are used as is, and bf16 inputs are
- * passed as their exact float32 widening, so every input value reaches the
+ * Inputs are float arrays: fp32 inputs are used as is, and bf16 / fp16
+ * inputs are passed as their exact float32 widening, so every input value reaches the
  * fp64 arithmetic exactly.  Build without -ffast-math.
  */
 #include <math.h>
@@ -103,19 +107,22 @@ static void oracle_row(const float* qi, const float* kbh, const float* vbh,
 }
 
 /*
- * q: [B,H,M,D], k and v: [B,H,N,D], all contiguous row-major floats.
+ * q: [B,H,M,D], k and v: [B,Hk,N,D], all contiguous row-major floats;
+ * H % Hk == 0 (Hk >= 1).
  * rows == NULL: every query row; o is [B,H,M,D] and lse is [B,H,M].
  * rows != NULL: only the n_rows listed rows (each in [0, M)), the same rows
  *   for every (b,h); o is [B,H,n_rows,D] and lse is [B,H,n_rows].
  * n_threads <= 0 uses the OpenMP default.
  * Returns 0 on success, nonzero on invalid arguments or allocation failure.
  */
-int fa2_oracle_fwd(const float* q, const float* k, const float* v, double* o,
-                   double* lse, int64_t B, int64_t H, int64_t M, int64_t N,
-                   int64_t D, double scale, int causal, const int64_t* rows,
-                   int64_t n_rows, int n_threads) {
+int fa2_oracle_fwd_gqa(const float* q, const float* k, const float* v, double* o,
+                       double* lse, int64_t B, int64_t H, int64_t Hk, int64_t M,
+                       int64_t N, int64_t D, double scale, int causal,
+                       const int64_t* rows, int64_t n_rows, int n_threads) {
     if (!q || !k || !v || !o || !lse) return FA2_ORACLE_EINVAL;
     if (B < 0 || H < 0 || M < 0 || N <= 0 || D <= 0) return FA2_ORACLE_EINVAL;
+    if (Hk < 1 || H % Hk != 0) return FA2_ORACLE_EINVAL;
+    const int64_t group = H / Hk;  /* query heads per K/V head */
     const int64_t R = rows ? n_rows : M;
     if (R < 0) return FA2_ORACLE_EINVAL;
     if (rows) {
@@ -146,11 +153,22 @@ int fa2_oracle_fwd(const float* q, const float* k, const float* v, double* o,
             const int64_t bh = t / R;
             const int64_t r = t % R;
             const int64_t i = rows ? rows[r] : r;
-            oracle_row(q + (bh * M + i) * D, k + bh * N * D, v + bh * N * D,
+            const int64_t b = bh / H, h = bh % H;
+            const int64_t kvh = b * Hk + h / group; /* (hk) */
+            oracle_row(q + (bh * M + i) * D, k + kvh * N * D, v + kvh * N * D,
                        o + (bh * R + r) * D, lse + bh * R + r, i, N, D, scale,
                        causal, s);
         }
         free(s);
     }
     return status;
+}
+
+/* Multi-head attention: every query head has its own K/V head (Hk == H). */
+int fa2_oracle_fwd(const float* q, const float* k, const float* v, double* o,
+                   double* lse, int64_t B, int64_t H, int64_t M, int64_t N,
+                   int64_t D, double scale, int causal, const int64_t* rows,
+                   int64_t n_rows, int n_threads) {
+    return fa2_oracle_fwd_gqa(q, k, v, o, lse, B, H, H > 0 ? H : 1, M, N, D,
+                              scale, causal, rows, n_rows, n_threads);
 }

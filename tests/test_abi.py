@@ -122,3 +122,68 @@ def test_single_hip_runtime_in_process():
     # from torch.  A second runtime copy would make every launch fail.
     import torch  # noqa: F401
     assert len(fa2._hip_runtimes_mapped()) <= 1, fa2._hip_runtimes_mapped()
+
+
+# --------------------------------------------------- fa2_fwd_ex (no launches)
+
+def call_ex(H=4, Hk=4, M=16, N=16, D=64, n_splits=1, ws=None, ws_size=0, dtype=None, causal=0):
+    dtype = fa2.FA2_DTYPE_F32 if dtype is None else dtype
+    return fa2.fa2_fwd_ex(Q, K, V, O, L, 1, H, Hk, M, N, D, 0.125, causal, dtype, n_splits, ws, ws_size, None)
+
+
+@pytest.mark.parametrize("H,Hk", [(4, 0), (4, 3), (4, 8), (4, -1)])
+def test_ex_rejects_bad_kv_head_count(H, Hk):
+    assert call_ex(H=H, Hk=Hk) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("n_splits", [-1, fa2.FA2_MAX_SPLITS + 1])
+def test_ex_rejects_bad_split_count(n_splits):
+    assert call_ex(n_splits=n_splits) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+def test_ex_split_needs_a_workspace():
+    W = 8 * A
+    need = fa2.fa2_fwd_workspace_bytes(1, 4, 16, 64, 3)
+    assert call_ex(n_splits=3) == fa2.FA2_ERR_INVALID_ARGUMENT                       # none
+    assert call_ex(n_splits=3, ws=W, ws_size=need - 1) == fa2.FA2_ERR_INVALID_ARGUMENT  # short
+    assert call_ex(n_splits=3, ws=W + 8, ws_size=need) == fa2.FA2_ERR_INVALID_ARGUMENT  # misaligned
+    assert call_ex(n_splits=3, ws=O - 64, ws_size=need) == fa2.FA2_ERR_INVALID_ARGUMENT  # overlaps o
+    assert call_ex(n_splits=3, ws=W, ws_size=-5) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+def test_ex_empty_problem_needs_no_launch():
+    # M == 0 with a valid split request: checks pass, nothing is enqueued
+    W = 8 * A
+    assert call_ex(M=0, n_splits=4, ws=W, ws_size=1 << 20) == fa2.FA2_OK
+    assert call_ex(H=0, Hk=1) == fa2.FA2_OK
+
+
+def test_ex_checks_kv_overlap_with_hk_sized_buffers():
+    # k, v hold B*Hk*N*D elements: o placed right after a 1-head K is fine,
+    # inside it is not
+    kv_bytes = 1 * 1 * 16 * 64 * 4
+    st = fa2.fa2_fwd_ex(Q, K, V, K + kv_bytes // 2, L, 1, 4, 1, 16, 16, 64, 0.125, 0,
+                        fa2.FA2_DTYPE_F32, 1, None, 0, None)
+    assert st == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_bytes():
+    assert fa2.fa2_fwd_workspace_bytes(2, 3, 10, 64, 1) == 0
+    rows = 4 * 2 * 3 * 10
+    assert fa2.fa2_fwd_workspace_bytes(2, 3, 10, 64, 4) == -(-rows * 64 * 4 // 256) * 256 + rows * 4
+    assert fa2.fa2_fwd_workspace_bytes(2, 3, 10, 64, 0) == -1
+    assert fa2.fa2_fwd_workspace_bytes(-1, 3, 10, 64, 2) == -1
+    assert fa2.fa2_fwd_workspace_bytes(1, 1, 1, 64, fa2.FA2_MAX_SPLITS + 1) == -1
+
+
+def test_num_splits_heuristic():
+    bf16 = fa2.FA2_DTYPE_BF16
+    # a grid that already fills the GPU is never split
+    assert fa2.fa2_fwd_num_splits(4, 16, 4096, 4096, 128, 1, bf16) == 1
+    # decode-like: one query tile per head, many keys
+    s = fa2.fa2_fwd_num_splits(1, 8, 1, 8192, 128, 0, bf16)
+    assert 1 < s <= fa2.FA2_MAX_SPLITS and s <= (8192 // 64) // 2
+    # few keys: at least two K/V tiles per split
+    assert fa2.fa2_fwd_num_splits(1, 1, 1, 128, 128, 0, bf16) == 1
+    # arguments the entry point would reject
+    assert fa2.fa2_fwd_num_splits(1, 1, 1, 128, 96, 0, bf16) == 1

@@ -188,6 +188,45 @@ def check_slices_independent(attn):
             np.testing.assert_array_equal(lse[b, h], l1[0, 0])
 
 
+# ------------------------------------------------------ grouped-query heads
+
+def check_gqa_equals_expanded_heads(attn):
+    # Query head h reads K/V head h // G: giving every query head its own copy
+    # of that K/V head must not change anything.
+    for Hk in (1, 2, 3):
+        q = rnd((2, 6, 21, 64), 60 + Hk)
+        k, v = rnd((2, Hk, 33, 64), 61 + Hk), rnd((2, Hk, 33, 64), 62 + Hk)
+        G = 6 // Hk
+        for causal in (False, True):
+            o, lse = attn(q, k, v, 0.3, causal)
+            o2, l2 = attn(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), 0.3, causal)
+            np.testing.assert_array_equal(o, o2)
+            np.testing.assert_array_equal(lse, l2)
+
+
+def check_mqa_constant_scores(attn):
+    # One K/V head for all query heads and Q = 0: every head of batch b
+    # returns the mean of V[b, 0] and L = log N.
+    q = np.zeros((2, 4, 5, 64), np.float32)
+    k, v = rnd((2, 1, 29, 64), 63), rnd((2, 1, 29, 64), 64)
+    o, lse = attn(q, k, v, 0.125, False)
+    mean = v.astype(np.float64).mean(axis=2, keepdims=True)  # [2, 1, 1, 64]
+    close(o, np.broadcast_to(mean, o.shape), 1e-14)
+    close(lse, math.log(29), 1e-14)
+
+
+def check_gqa_torch(attn):
+    # torch fp64 SDPA on K/V expanded with repeat_interleave along heads
+    q = rnd((1, 8, 40, 64), 65)
+    k, v = rnd((1, 2, 50, 64), 66), rnd((1, 2, 50, 64), 67)
+    o, lse = attn(q, k, v, 0.125, True)
+    ke = torch.from_numpy(k).repeat_interleave(4, dim=1).numpy()
+    ve = torch.from_numpy(v).repeat_interleave(4, dim=1).numpy()
+    o_ref, l_ref = torch_reference(q, ke, ve, 0.125, True)
+    close(o, o_ref, 1e-12)
+    close(lse, l_ref, 1e-12)
+
+
 # --------------------------------------------------------- library special case
 
 def torch_reference(q, k, v, scale, causal):
@@ -339,6 +378,26 @@ def test_matches_decimal_brute_force(M, N, D, causal):
     check_brute(oracle.attention, M, N, D, causal)
 
 
+def test_gqa_equals_expanded_heads():
+    check_gqa_equals_expanded_heads(oracle.attention)
+
+
+def test_mqa_constant_scores():
+    check_mqa_constant_scores(oracle.attention)
+
+
+def test_gqa_matches_torch():
+    check_gqa_torch(oracle.attention)
+
+
+def test_fp16_inputs_are_widened_exactly():
+    q, k, v = (torch.from_numpy(rnd((1, 2, 30, 64), s)).to(torch.float16) for s in (70, 71, 72))
+    o, lse = oracle.attention(q, k, v, 0.125, True)
+    o2, l2 = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), 0.125, True)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, l2)
+
+
 def test_sampled_rows_equal_full_rows():
     q, k, v = rnd((1, 2, 90, 64), 33), rnd((1, 2, 90, 64), 34), rnd((1, 2, 90, 64), 35)
     rows = np.array([0, 5, 44, 89], np.int64)
@@ -355,6 +414,10 @@ def test_invalid_arguments_raise():
         oracle.attention(q, empty, empty, 1.0, False)
     with pytest.raises(ValueError):
         oracle.attention(q, q, q, 1.0, False, rows=np.array([4], np.int64))
+    q3 = rnd((1, 3, 4, 64), 37)
+    kv2 = rnd((1, 2, 4, 64), 38)
+    with pytest.raises(ValueError):  # 3 query heads cannot share 2 K/V heads
+        oracle.attention(q3, kv2, kv2, 1.0, False)
 
 
 # ------------------------------------------------------- planted-mistake check
@@ -362,7 +425,8 @@ def test_invalid_arguments_raise():
 ALL_PINS = (
     [check_single_key, check_causal_prefix_means, check_causal_row_zero, check_weights_sum_to_one,
      check_identity_values, check_large_magnitude_two_keys, check_key_shift,
-     check_joint_key_permutation, check_linear_in_values, check_slices_independent]
+     check_joint_key_permutation, check_linear_in_values, check_slices_independent,
+     check_gqa_equals_expanded_heads, check_mqa_constant_scores, check_gqa_torch]
     + [lambda a, N=N: check_constant_scores(a, N) for N in (1, 37, 65)]
     + [lambda a, c=c: check_geometric_scores(a, c) for c in (0.05, 0.7)]
     + [lambda a, s=s, c=c: check_torch(a, *s, c) for s in LIB_SHAPES[:4] for c in (False, True)]
@@ -379,6 +443,7 @@ MUTANTS = {
     "no normalisation": ("orow[d] /= l;", "orow[d] /= 1.0;"),
     "weights misaligned with values": ("const double e = s[j];", "const double e = s[n_vis - 1 - j];"),
     "key row misindexed": ("const float* kj = kbh + j * D;", "const float* kj = kbh + (n_vis - 1 - j) * D;"),
+    "kv head misindexed": ("const int64_t kvh = b * Hk + h / group;", "const int64_t kvh = b * Hk + h % Hk;"),
     "last key dropped": ("for (int64_t j = 0; j < n_vis; ++j) {\n        s[j] = exp", "for (int64_t j = 0; j + 1 < n_vis; ++j) {\n        s[j] = exp"),
 }
 

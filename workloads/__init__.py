@@ -36,7 +36,7 @@ class Workload:
     M: int
     N: int
     D: int
-    dtype: str          # "f32" or "bf16"
+    dtype: str          # "f32", "bf16" or "f16"
     causal: bool
     qk_sigma: float = 1.0
     v_sigma: float = 1.0
@@ -97,17 +97,19 @@ def get(name: str) -> Workload:
 
 
 def torch_dtype(dtype: str) -> torch.dtype:
-    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
 
 
 def make_inputs(B: int, H: int, M: int, N: int, D: int, dtype: str = "f32", seed: int = 0,
-                qk_sigma: float = 1.0, v_sigma: float = 1.0):
-    """Draw (q, k, v) on the CPU, contiguous, in the I/O dtype."""
+                qk_sigma: float = 1.0, v_sigma: float = 1.0, Hk: int | None = None):
+    """Draw (q, k, v) on the CPU, contiguous, in the I/O dtype (rounded to
+    nearest even from fp32 draws).  k and v have Hk heads (default H)."""
+    Hk = H if Hk is None else Hk
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
     q = torch.randn((B, H, M, D), generator=g, dtype=torch.float32)
-    k = torch.randn((B, H, N, D), generator=g, dtype=torch.float32)
-    v = torch.randn((B, H, N, D), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hk, N, D), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hk, N, D), generator=g, dtype=torch.float32)
     if qk_sigma != 1.0:
         q.mul_(qk_sigma)
         k.mul_(qk_sigma)
