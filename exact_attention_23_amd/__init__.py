@@ -17,13 +17,14 @@ import ctypes
 import math
 import os
 
-__all__ = ["FA2_DTYPE_F32", "FA2_DTYPE_BF16", "FA2_OK", "FA2_ERR_INVALID_ARGUMENT",
+__all__ = ["FA2_DTYPE_F32", "FA2_DTYPE_BF16", "FA2_DTYPE_F16", "FA2_OK", "FA2_ERR_INVALID_ARGUMENT",
            "FA2_ERR_UNSUPPORTED", "FA2_ERR_LAUNCH", "FA2_ERR_NO_DEVICE", "FA2_MAX_SPLITS", "Fa2Error",
            "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_workspace_bytes", "fa2_fwd_num_splits",
            "fa2_status_string", "forward", "library_path", "EXPORTED_SYMBOLS"]
 
 FA2_DTYPE_F32 = 0
 FA2_DTYPE_BF16 = 1
+FA2_DTYPE_F16 = 2
 
 FA2_OK = 0
 FA2_ERR_INVALID_ARGUMENT = 1
@@ -138,7 +139,9 @@ def _dtype_code(t):
         return FA2_DTYPE_F32
     if t.dtype == torch.bfloat16:
         return FA2_DTYPE_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    if t.dtype == torch.float16:
+        return FA2_DTYPE_F16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32, bfloat16 or float16")
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
@@ -146,7 +149,7 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     """Attention forward on the current CUDA/HIP stream.
 
     q: [B,H,M,D], k/v: [B,Hk,N,D] contiguous device tensors of one dtype
-    (float32 or bfloat16), H % Hk == 0 (query head h reads K/V head
+    (float32, bfloat16 or float16), H % Hk == 0 (query head h reads K/V head
     h // (H // Hk)).  Returns (o [B,H,M,D] in q's dtype, lse [B,H,M]
     float32).  ``scale`` defaults to 1/sqrt(D).  ``n_splits``: 1 = one kernel
     over all keys, 0 = library's choice, >1 = split K/V with a combine kernel;

@@ -47,7 +47,7 @@
 //    fastest-varying grid index so that all tiles of one head land on the same
 //    XCD (workgroups are dealt to the 8 XCDs round-robin).
 //  * bf16 at D = 128 uses a ping-pong schedule between two groups of four
-//    waves (see fa2_fwd_bf16_pp_kernel), because a wave's own MFMA and VALU
+//    waves (see fa2_fwd_half_pp_kernel), because a wave's own MFMA and VALU
 //    work does not overlap on gfx950 while two waves on one SIMD do.
 
 #include <hip/hip_runtime.h>
@@ -131,9 +131,43 @@ __device__ __forceinline__ float xchg_half(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    // one v_cvt_pk_bf16_f32: both halves rounded to nearest even
-    const __bf16 __attribute__((ext_vector_type(2))) v = {(__bf16)lo, (__bf16)hi};
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The 16-bit input types share every kernel; they differ only in the MFMA
+// opcode, the conversion that rounds P and O (to nearest even in both), and
+// the packed sum of two rounded weights.
+template <typename E>
+struct Half;
+template <>
+struct Half<__bf16> {
+    using v8 = bf16x8;
+    using v2 = bf16x2;
+    static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float sum2(v2 p, float acc) {  // acc + p.x + p.y
+        const v2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
+    }
+};
+template <>
+struct Half<_Float16> {
+    using v8 = f16x8;
+    using v2 = f16x2;
+    static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float sum2(v2 p, float acc) {
+        const v2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(p, one, acc, false);
+    }
+};
+
+// Two floats rounded to nearest even and packed (one v_cvt_pk_*_f32).
+template <typename E>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    const typename Half<E>::v2 v = {(E)lo, (E)hi};
     return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -214,7 +248,7 @@ __device__ __forceinline__ float* partial_l(const FwdParams& p, const WgTask& t,
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel
+// 16-bit kernel (bf16 or fp16 inputs, E)
 // ---------------------------------------------------------------------------
 // D: head dim (64 or 128); BN: keys per K/V tile (multiple of 32);
 // NW: waves per workgroup; QB: 32-query blocks per wave.
@@ -232,7 +266,7 @@ __device__ __forceinline__ float* partial_l(const FwdParams& p, const WgTask& t,
 //    transposition in LDS; chunk ^= f_V(row) keeps the 4 rows x 64 bytes a
 //    half-wave reads in distinct banks.
 template <int D, int BN, int NW, int QB>
-struct Bf16Traits {
+struct HalfTraits {
     static constexpr int kThreads = NW * 64;
     static constexpr int kQPW = 32 * QB;          // query rows per wave
     static constexpr int kBM = kQPW * NW;         // query rows per workgroup
@@ -265,17 +299,18 @@ __device__ __forceinline__ int swz_v(int r) {
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-__device__ constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-template <int D, int BN, int NW, int QB, int WAVES_PER_SIMD, bool CAUSAL, bool SPLIT>
+template <typename E, int D, int BN, int NW, int QB, int WAVES_PER_SIMD, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64, WAVES_PER_SIMD)
-fa2_fwd_bf16_kernel(const FwdParams p) {
-    using T = Bf16Traits<D, BN, NW, QB>;
-    const __bf16* __restrict__ Q = static_cast<const __bf16*>(p.q);
-    const __bf16* __restrict__ K = static_cast<const __bf16*>(p.k);
-    const __bf16* __restrict__ V = static_cast<const __bf16*>(p.v);
-    __bf16* __restrict__ O = static_cast<__bf16*>(p.o);
+fa2_fwd_half_kernel(const FwdParams p) {
+    using T = HalfTraits<D, BN, NW, QB>;
+    using V8 = typename Half<E>::v8;
+    using V2 = typename Half<E>::v2;
+    const E* __restrict__ Q = static_cast<const E*>(p.q);
+    const E* __restrict__ K = static_cast<const E*>(p.k);
+    const E* __restrict__ V = static_cast<const E*>(p.v);
+    E* __restrict__ O = static_cast<E*>(p.o);
     float* __restrict__ LSE = p.lse;
     const int M = p.M, N = p.N;
     const float c_log2 = p.c_log2;
@@ -299,9 +334,9 @@ fa2_fwd_bf16_kernel(const FwdParams p) {
     const int bh = task.bh;
     const int qw0 = task.qt * T::kBM + wave * T::kQPW;  // first query row of this wave
 
-    const __bf16* Qh = Q + (int64_t)bh * M * D;
-    const __bf16* Kh = K + (int64_t)task.bkv * N * D;
-    const __bf16* Vh = V + (int64_t)task.bkv * N * D;
+    const E* Qh = Q + (int64_t)bh * M * D;
+    const E* Kh = K + (int64_t)task.bkv * N * D;
+    const E* Vh = V + (int64_t)task.bkv * N * D;
 
     // local tile kt is K/V tile kv_t0 + kt of the head
     const int kv_t0 = task.t_begin;
@@ -309,16 +344,16 @@ fa2_fwd_bf16_kernel(const FwdParams p) {
     const int n_kv_wave = wave_tiles<CAUSAL>(p, task, qw0, T::kQPW, BN);
 
     // ---- Q fragments: B operand of S^T = K Q^T (lane = query, 8 d values)
-    bf16x8 qf[QB][T::kDS];
+    V8 qf[QB][T::kDS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int row = qw0 + 32 * qb + l32;
 #pragma unroll
         for (int s = 0; s < T::kDS; ++s) {
             if (row < M) {
-                qf[qb][s] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)row * D + 16 * s + 8 * h);
+                qf[qb][s] = *reinterpret_cast<const V8*>(Qh + (int64_t)row * D + 16 * s + 8 * h);
             } else {
-                qf[qb][s] = bf16x8{};
+                qf[qb][s] = V8{};
             }
         }
     }
@@ -383,16 +418,16 @@ fa2_fwd_bf16_kernel(const FwdParams p) {
         for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = floatx16{};
-        bf16x8 kf[2][T::kKB];
+        V8 kf[2][T::kKB];
 #pragma unroll
         for (int kb = 0; kb < T::kKB; ++kb)
-            kf[0][kb] = *reinterpret_cast<const bf16x8*>(klds + 32 * kb * T::kRowBytes + k_lane_off[0]);
+            kf[0][kb] = *reinterpret_cast<const V8*>(klds + 32 * kb * T::kRowBytes + k_lane_off[0]);
 #pragma unroll
         for (int s = 0; s < T::kDS; ++s) {
             if (s + 1 < T::kDS) {
 #pragma unroll
                 for (int kb = 0; kb < T::kKB; ++kb)
-                    kf[(s + 1) & 1][kb] = *reinterpret_cast<const bf16x8*>(
+                    kf[(s + 1) & 1][kb] = *reinterpret_cast<const V8*>(
                         klds + 32 * kb * T::kRowBytes + k_lane_off[s + 1]);
             }
             // keep the next step's reads ahead of this step's MFMAs
@@ -401,7 +436,7 @@ fa2_fwd_bf16_kernel(const FwdParams p) {
             for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][kb], qf[qb][s], sacc[kb][qb], 0, 0, 0);
+                    sacc[kb][qb] = Half<E>::mfma(kf[s & 1][kb], qf[qb][s], sacc[kb][qb]);
         }
 
         // boundary tiles only: keys past N, and (causal) keys after the
@@ -422,7 +457,7 @@ fa2_fwd_bf16_kernel(const FwdParams p) {
             }
         }
 
-        bf16x8 pf[T::kKB][2][QB];  // P^T as B operands of the PV MFMAs
+        V8 pf[T::kKB][2][QB];  // P^T as B operands of the PV MFMAs
         // Online softmax in the log2 domain.  The running max is only moved
         // (and O, l rescaled) when some row's max grew by more than 8 (a factor
         // 256); otherwise P = exp2(s*c - m_run) <= 256, which the fp32 O and l
@@ -469,10 +504,10 @@ fa2_fwd_bf16_kernel(const FwdParams p) {
                     for (int t = 0; t < 8; t += 2) {
                         const float p0 = fast_exp2(fmaf(sacc[kb][qb][8 * ms + t], c_log2, -m_use));
                         const float p1 = fast_exp2(fmaf(sacc[kb][qb][8 * ms + t + 1], c_log2, -m_use));
-                        const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+                        const V2 pp = {(E)p0, (E)p1};
                         pf[kb][ms][qb][t] = pp[0];
                         pf[kb][ms][qb][t + 1] = pp[1];
-                        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, lsum, false);
+                        lsum = Half<E>::sum2(pp, lsum);
                         esum += p0;
                         esum += p1;
                     }
@@ -487,9 +522,9 @@ fa2_fwd_bf16_kernel(const FwdParams p) {
             const char* p0 = vlds + 16 * step * T::kRowBytes + v_lane_off[db];
             const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
             const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 8 * T::kRowBytes));
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        bf16x8 vf[2][T::kDB];
+        V8 vf[2][T::kDB];
 #pragma unroll
         for (int db = 0; db < T::kDB; ++db) vf[0][db] = read_v(0, db);
 #pragma unroll
@@ -503,7 +538,7 @@ fa2_fwd_bf16_kernel(const FwdParams p) {
             for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[step & 1][db], pf[kb][ms][qb], oacc[db][qb], 0, 0, 0);
+                    oacc[db][qb] = Half<E>::mfma(vf[step & 1][db], pf[kb][ms][qb], oacc[db][qb]);
         }
     };
 
@@ -556,15 +591,15 @@ fa2_fwd_bf16_kernel(const FwdParams p) {
                     }
                 if (h == 0) *partial_l(p, task, query) = lse;
             } else {
-                __bf16* orow = O + ((int64_t)bh * M + query) * D;
+                E* orow = O + ((int64_t)bh * M + query) * D;
 #pragma unroll
                 for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int d = 32 * db + 8 * g + 4 * h;
                         uint32_t w[2];
-                        w[0] = pack_bf16x2(oacc[db][qb][4 * g + 0] * inv, oacc[db][qb][4 * g + 1] * inv);
-                        w[1] = pack_bf16x2(oacc[db][qb][4 * g + 2] * inv, oacc[db][qb][4 * g + 3] * inv);
+                        w[0] = pack2<E>(oacc[db][qb][4 * g + 0] * inv, oacc[db][qb][4 * g + 1] * inv);
+                        w[1] = pack2<E>(oacc[db][qb][4 * g + 2] * inv, oacc[db][qb][4 * g + 3] * inv);
                         *reinterpret_cast<uint2*>(orow + d) = make_uint2(w[0], w[1]);
                     }
                 if (h == 0) LSE[(int64_t)bh * M + query] = lse;
@@ -574,7 +609,7 @@ fa2_fwd_bf16_kernel(const FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel, ping-pong schedule
+// 16-bit kernel, ping-pong schedule
 // ---------------------------------------------------------------------------
 // On gfx950 a wave's own MFMA and VALU instructions do not overlap, but the
 // MFMA of one wave and the VALU of another wave on the same SIMD do.  This
@@ -618,14 +653,16 @@ struct PPTraits {
     static_assert(kTileChunks % (64 * kNW) == 0, "loader split");
 };
 
-template <int D, int BN, bool CAUSAL, bool SPLIT>
+template <typename E, int D, int BN, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(512, 2)
-fa2_fwd_bf16_pp_kernel(const FwdParams p) {
+fa2_fwd_half_pp_kernel(const FwdParams p) {
     using T = PPTraits<D, BN>;
-    const __bf16* __restrict__ Q = static_cast<const __bf16*>(p.q);
-    const __bf16* __restrict__ K = static_cast<const __bf16*>(p.k);
-    const __bf16* __restrict__ V = static_cast<const __bf16*>(p.v);
-    __bf16* __restrict__ O = static_cast<__bf16*>(p.o);
+    using V8 = typename Half<E>::v8;
+    using V2 = typename Half<E>::v2;
+    const E* __restrict__ Q = static_cast<const E*>(p.q);
+    const E* __restrict__ K = static_cast<const E*>(p.k);
+    const E* __restrict__ V = static_cast<const E*>(p.v);
+    E* __restrict__ O = static_cast<E*>(p.o);
     float* __restrict__ LSE = p.lse;
     const int M = p.M, N = p.N;
     const float c_log2 = p.c_log2;
@@ -645,9 +682,9 @@ fa2_fwd_bf16_pp_kernel(const FwdParams p) {
     const int bh = task.bh;
     const int qw0 = task.qt * T::kBM + 32 * (2 * (wave & 3) + grp);  // first query row of this wave
 
-    const __bf16* Qh = Q + (int64_t)bh * M * D;
-    const __bf16* Kh = K + (int64_t)task.bkv * N * D;
-    const __bf16* Vh = V + (int64_t)task.bkv * N * D;
+    const E* Qh = Q + (int64_t)bh * M * D;
+    const E* Kh = K + (int64_t)task.bkv * N * D;
+    const E* Vh = V + (int64_t)task.bkv * N * D;
 
     // local tile t is K/V tile kv_t0 + t of the head
     const int kv_t0 = task.t_begin;
@@ -655,13 +692,13 @@ fa2_fwd_bf16_pp_kernel(const FwdParams p) {
     const int n_w = wave_tiles<CAUSAL>(p, task, qw0, 32, BN);  // tiles this wave needs
 
     // ---- Q fragments: B operand of S^T = K Q^T (lane = query, 8 d values)
-    bf16x8 qf[T::kDS];
+    V8 qf[T::kDS];
     {
         const int row = qw0 + l32;
 #pragma unroll
         for (int s = 0; s < T::kDS; ++s)
-            qf[s] = row < M ? *reinterpret_cast<const bf16x8*>(Qh + (int64_t)row * D + 16 * s + 8 * h)
-                            : bf16x8{};
+            qf[s] = row < M ? *reinterpret_cast<const V8*>(Qh + (int64_t)row * D + 16 * s + 8 * h)
+                            : V8{};
     }
 
     // Running state of this lane's query row: O^T, the max m (log2 units),
@@ -672,9 +709,9 @@ fa2_fwd_bf16_pp_kernel(const FwdParams p) {
     for (int db = 0; db < T::kDB; ++db) oacc[db] = floatx16{};
     float m_run = -INFINITY, l_run = 0.f, l_exact = 0.f;
     floatx16 sacc[T::kKB];        // S^T of the tile between its S and sm phases
-    bf16x8 pf[T::kKB][2];         // P^T of the tile between its sm and PV phases
+    V8 pf[T::kKB][2];         // P^T of the tile between its sm and PV phases
 #pragma unroll
-    for (int kb = 0; kb < T::kKB; ++kb) pf[kb][0] = pf[kb][1] = bf16x8{};
+    for (int kb = 0; kb < T::kKB; ++kb) pf[kb][0] = pf[kb][1] = V8{};
 
     // ---- async tile copies (same chunk assignment as the kernel above)
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -686,7 +723,7 @@ fa2_fwd_bf16_pp_kernel(const FwdParams p) {
         cp_koff[i] = (uint32_t)(r * T::kRowBytes + 16 * (p ^ swz_k<D>(r)));
         cp_voff[i] = (uint32_t)(r * T::kRowBytes + 16 * (p ^ swz_v<D>(r)));
     }
-    auto issue_copy = [&](const __bf16* head, const uint32_t* cp_off, int kt, char* dst) {
+    auto issue_copy = [&](const E* head, const uint32_t* cp_off, int kt, char* dst) {
         copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(head, cp_off, wave_u, kv_t0 + kt, N, dst);
     };
 
@@ -718,18 +755,18 @@ fa2_fwd_bf16_pp_kernel(const FwdParams p) {
         const char* p0 = vprev + 16 * step * T::kRowBytes + v_lane_off[db];
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 8 * T::kRowBytes));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     auto read_k = [&](const char* klds, int i) {
         const int s = i / T::kKB, kb = i % T::kKB;
-        return *reinterpret_cast<const bf16x8*>(klds + 32 * kb * T::kRowBytes + k_lane_off[s]);
+        return *reinterpret_cast<const V8*>(klds + 32 * kb * T::kRowBytes + k_lane_off[s]);
     };
     auto mfma_phase = [&](int t, const char* klds, const char* vprev) {
         if (t > n_w) return;
 #pragma unroll
         for (int kb = 0; kb < T::kKB; ++kb) sacc[kb] = floatx16{};
         constexpr int kAhead = 2;
-        bf16x8 vr[kAhead + 1], kr[kAhead + 1];
+        V8 vr[kAhead + 1], kr[kAhead + 1];
 #pragma unroll
         for (int i = 0; i < kAhead; ++i) {
             vr[i] = read_v(vprev, i);
@@ -744,12 +781,12 @@ fa2_fwd_bf16_pp_kernel(const FwdParams p) {
             __builtin_amdgcn_sched_barrier(0);
             {
                 const int step = i / T::kDB, db = i % T::kDB;
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % (kAhead + 1)], pf[step >> 1][step & 1],
-                                                                   oacc[db], 0, 0, 0);
+                oacc[db] = Half<E>::mfma(vr[i % (kAhead + 1)], pf[step >> 1][step & 1],
+                                                                   oacc[db]);
             }
             {
                 const int s = i / T::kKB, kb = i % T::kKB;
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % (kAhead + 1)], qf[s], sacc[kb], 0, 0, 0);
+                sacc[kb] = Half<E>::mfma(kr[i % (kAhead + 1)], qf[s], sacc[kb]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -814,10 +851,10 @@ fa2_fwd_bf16_pp_kernel(const FwdParams p) {
                     const int c = (u >> 1) & 3;
                     const float p0 = fast_exp2(fmaf(sacc[kb][8 * ms + u], c_log2, -m_use));
                     const float p1 = fast_exp2(fmaf(sacc[kb][8 * ms + u + 1], c_log2, -m_use));
-                    const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+                    const V2 pp = {(E)p0, (E)p1};
                     pf[kb][ms][u] = pp[0];
                     pf[kb][ms][u + 1] = pp[1];
-                    lsum[c] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, lsum[c], false);
+                    lsum[c] = Half<E>::sum2(pp, lsum[c]);
                     esum[c] += p0 + p1;
                 }
         l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
@@ -883,14 +920,14 @@ fa2_fwd_bf16_pp_kernel(const FwdParams p) {
                     }
                 if (h == 0) *partial_l(p, task, query) = lse;
             } else {
-                __bf16* orow = O + ((int64_t)bh * M + query) * D;
+                E* orow = O + ((int64_t)bh * M + query) * D;
 #pragma unroll
                 for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int d = 32 * db + 8 * g + 4 * h;
-                        const uint32_t w0 = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-                        const uint32_t w1 = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+                        const uint32_t w0 = pack2<E>(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+                        const uint32_t w1 = pack2<E>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
                         *reinterpret_cast<uint2*>(orow + d) = make_uint2(w0, w1);
                     }
                 if (h == 0) LSE[(int64_t)bh * M + query] = lse;
@@ -1144,7 +1181,7 @@ fa2_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_l,
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     OutT* dst = O + (int64_t)row * D + lane * kPer;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) dst[i] = static_cast<OutT>(acc[i] * inv);  // bf16: nearest even
+    for (int i = 0; i < kPer; ++i) dst[i] = static_cast<OutT>(acc[i] * inv);  // bf16, fp16: nearest even
     if (lane == 0) LSE[row] = m == -INFINITY ? -INFINITY : m + fast_log2(wsum) * kLn2;
 }
 
@@ -1166,12 +1203,16 @@ struct Entry {
 #define FWD_KERNEL(...) reinterpret_cast<const void*>(&__VA_ARGS__)
 #define FWD_PAIR(name, ...) FWD_KERNEL(name<__VA_ARGS__, false>), FWD_KERNEL(name<__VA_ARGS__, true>)
 const Entry kTable[] = {
-    // bf16: 8 waves (two per SIMD) share each K/V tile; 256 query rows per
+    // bf16, fp16: 8 waves (two per SIMD) share each K/V tile; 256 query rows per
     // workgroup; 64-key tiles at D=128, 128-key tiles at D=64 (measured best)
-    {FA2_DTYPE_BF16, 64, 0, FWD_PAIR(fa2_fwd_bf16_kernel, 64, 128, 8, 1, 2, false), 512, 256, 128, 1},
-    {FA2_DTYPE_BF16, 64, 1, FWD_PAIR(fa2_fwd_bf16_kernel, 64, 128, 8, 1, 2, true), 512, 256, 128, 1},
-    {FA2_DTYPE_BF16, 128, 0, FWD_PAIR(fa2_fwd_bf16_pp_kernel, 128, 64, false), 512, 256, 64, 1},
-    {FA2_DTYPE_BF16, 128, 1, FWD_PAIR(fa2_fwd_bf16_pp_kernel, 128, 64, true), 512, 256, 64, 1},
+    {FA2_DTYPE_BF16, 64, 0, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 64, 128, 8, 1, 2, false), 512, 256, 128, 1},
+    {FA2_DTYPE_BF16, 64, 1, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 64, 128, 8, 1, 2, true), 512, 256, 128, 1},
+    {FA2_DTYPE_BF16, 128, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 128, 64, false), 512, 256, 64, 1},
+    {FA2_DTYPE_BF16, 128, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 128, 64, true), 512, 256, 64, 1},
+    {FA2_DTYPE_F16, 64, 0, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 64, 128, 8, 1, 2, false), 512, 256, 128, 1},
+    {FA2_DTYPE_F16, 64, 1, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 64, 128, 8, 1, 2, true), 512, 256, 128, 1},
+    {FA2_DTYPE_F16, 128, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, false), 512, 256, 64, 1},
+    {FA2_DTYPE_F16, 128, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, true), 512, 256, 64, 1},
     {FA2_DTYPE_F32, 64, 0, FWD_PAIR(fa2_fwd_f32_kernel, 64, 64, 4, false), 256, 128, 64, 2},
     {FA2_DTYPE_F32, 64, 1, FWD_PAIR(fa2_fwd_f32_kernel, 64, 64, 4, true), 256, 128, 64, 2},
     {FA2_DTYPE_F32, 128, 0, FWD_PAIR(fa2_fwd_f32_kernel, 128, 32, 4, false), 256, 128, 32, 1},
@@ -1186,6 +1227,8 @@ struct MergeEntry {
 const MergeEntry kMergeTable[] = {
     {FA2_DTYPE_BF16, 64, FWD_KERNEL(fa2_merge_kernel<__bf16, 64>)},
     {FA2_DTYPE_BF16, 128, FWD_KERNEL(fa2_merge_kernel<__bf16, 128>)},
+    {FA2_DTYPE_F16, 64, FWD_KERNEL(fa2_merge_kernel<_Float16, 64>)},
+    {FA2_DTYPE_F16, 128, FWD_KERNEL(fa2_merge_kernel<_Float16, 128>)},
     {FA2_DTYPE_F32, 64, FWD_KERNEL(fa2_merge_kernel<float, 64>)},
     {FA2_DTYPE_F32, 128, FWD_KERNEL(fa2_merge_kernel<float, 128>)},
 };
@@ -1251,7 +1294,7 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
     if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARGUMENT;
     if (B < 0 || H < 0 || Hk < 1 || M < 0 || N <= 0 || D <= 0) return FA2_ERR_INVALID_ARGUMENT;
     if (H > 0 && (Hk > H || H % Hk != 0)) return FA2_ERR_INVALID_ARGUMENT;
-    if (dtype != FA2_DTYPE_F32 && dtype != FA2_DTYPE_BF16) return FA2_ERR_INVALID_ARGUMENT;
+    if (dtype != FA2_DTYPE_F32 && dtype != FA2_DTYPE_BF16 && dtype != FA2_DTYPE_F16) return FA2_ERR_INVALID_ARGUMENT;
     if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARGUMENT;
     if (!(scale > 0.f) || !isfinite(scale)) return FA2_ERR_INVALID_ARGUMENT;
     if (n_splits < 0 || n_splits > FA2_MAX_SPLITS) return FA2_ERR_INVALID_ARGUMENT;

@@ -34,7 +34,8 @@ extern "C" {
 /* Element type of q, k, v and o.  lse is always float32. */
 typedef enum {
     FA2_DTYPE_F32 = 0,  /* IEEE binary32 */
-    FA2_DTYPE_BF16 = 1  /* bfloat16 (1-8-7); o is rounded to nearest-even */
+    FA2_DTYPE_BF16 = 1, /* bfloat16 (1-8-7); o is rounded to nearest-even */
+    FA2_DTYPE_F16 = 2   /* IEEE binary16 (1-5-10); o is rounded to nearest-even */
 } fa2_dtype;
 
 typedef enum {

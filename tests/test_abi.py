@@ -83,7 +83,7 @@ def test_bad_scale_rejected(scale):
     assert call(scale=scale) == fa2.FA2_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("kw", [dict(dtype=2), dict(dtype=-1), dict(causal=2), dict(causal=-1)])
+@pytest.mark.parametrize("kw", [dict(dtype=3), dict(dtype=-1), dict(causal=2), dict(causal=-1)])
 def test_bad_enums_rejected(kw):
     assert call(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
 

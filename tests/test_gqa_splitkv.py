@@ -37,7 +37,7 @@ def check(B, H, Hk, M, N, D, dtype, causal, n_splits=1, seed=0, qk_sigma=1.0):
 
 # ------------------------------------------------------------ grouped query
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("H,Hk", [(8, 1), (8, 2), (6, 3)])
@@ -57,7 +57,7 @@ def test_gqa_equals_mha_on_repeated_heads():
 
 # ---------------------------------------------------------------- split K/V
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("n_splits", [2, 3, 8])
@@ -72,12 +72,13 @@ def test_split_kv_more_splits_than_tiles(causal, dtype):
     check(1, 2, 2, 70, 200, 64, dtype, causal, n_splits=50, seed=11)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("M", [1, 4, 37])
 def test_split_kv_decode_shapes_auto(M, dtype):
     # few query rows over many keys: the case split K/V exists for
     B, H, N, D = 2, 8, 4096, 128
-    splits = fa2.fa2_fwd_num_splits(B, H, M, N, D, 0, fa2.FA2_DTYPE_BF16 if dtype == "bf16" else fa2.FA2_DTYPE_F32)
+    code = {"f32": fa2.FA2_DTYPE_F32, "bf16": fa2.FA2_DTYPE_BF16, "f16": fa2.FA2_DTYPE_F16}[dtype]
+    splits = fa2.fa2_fwd_num_splits(B, H, M, N, D, 0, code)
     note(f"auto splits for M={M}: {splits}")
     assert splits > 1
     check(B, H, 2, M, N, D, dtype, False, n_splits=0, seed=M)

@@ -37,18 +37,18 @@ def call(q, k, v, o, lse, causal, dtype_code):
     assert st == fa2.FA2_OK, fa2.fa2_status_string(st)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("M,N,D", [(1, 1, 64), (100, 37, 128), (129, 200, 64), (1000, 3000, 64), (300, 300, 128)])
 def test_no_out_of_bounds_access(M, N, D, causal, dtype):
     B, H = 2, 3
     q, k, v = workloads.make_inputs(B, H, M, N, D, dtype, seed=M + N)
-    code = fa2.FA2_DTYPE_F32 if dtype == "f32" else fa2.FA2_DTYPE_BF16
+    code = {"f32": fa2.FA2_DTYPE_F32, "bf16": fa2.FA2_DTYPE_BF16, "f16": fa2.FA2_DTYPE_F16}[dtype]
     nan = float("nan")
     qf, dq = padded(q.cuda(), nan)
     kf, dk = padded(k.cuda(), nan)
     vf, dv = padded(v.cuda(), nan)
-    sentinel = -12288.0  # exact in bf16 and fp32
+    sentinel = -12288.0  # exact in bf16, fp16 and fp32
     of, do = padded(torch.empty_like(q, device="cuda"), sentinel)
     lf, dl = padded(torch.empty((B, H, M), dtype=torch.float32, device="cuda"), sentinel)
     print(f"case B={B} H={H} M={M} N={N} D={D} {dtype} causal={causal}", flush=True)
