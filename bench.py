@@ -71,12 +71,26 @@ def load_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
-def dominant_kernel(w) -> str:
-    """The one kernel fa2_fwd launches for this workload (the dispatch table
-    of the library: fp32 kernel, or the 16-bit kernel, ping-pong at D=128)."""
+def dominant_kernel(w, splits: int = 1) -> str:
+    """The forward kernel the library launches for this workload (its
+    dispatch table: fp32 kernel, or the 16-bit kernel, ping-pong at D=128),
+    followed by the combine kernel when the key range is split."""
     if w.dtype == "f32":
-        return "fa2_fwd_f32_kernel"
-    return "fa2_fwd_half_pp_kernel" if w.D == 128 else "fa2_fwd_half_kernel"
+        k = "fa2_fwd_f32_kernel"
+    else:
+        k = "fa2_fwd_half_pp_kernel" if w.D == 128 else "fa2_fwd_half_kernel"
+    return k + (f" x{splits} splits + fa2_merge_kernel" if splits > 1 else "")
+
+
+def roofline_of(w, seconds: float):
+    """(bound, achieved, peak, unit): MFMA-bound when the workload's counted
+    flop per algorithmic byte exceeds the ridge point of its dtype, else
+    HBM-bound (decode-like shapes)."""
+    peak = PEAK_TFLOPS[w.dtype]
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if w.flops / w.compulsory_bytes >= ridge:
+        return "mfma", w.flops / seconds / 1e12, peak, "TFLOP/s"
+    return "hbm", w.compulsory_bytes / seconds / 1e9, HBM_PEAK_GBS, "GB/s"
 
 
 def prewarm(fn, seconds: float):
@@ -239,20 +253,39 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
+    def code_of(w):
+        return {"f32": fa2.FA2_DTYPE_F32, "bf16": fa2.FA2_DTYPE_BF16, "f16": fa2.FA2_DTYPE_F16}[w.dtype]
+
+    def splits_of(w):
+        if w.n_splits != 0:
+            return w.n_splits
+        return fa2.fa2_fwd_num_splits(w.B, w.H, w.kv_heads, w.M, w.N, w.D, int(w.causal), code_of(w))
+
     def setup(w):
         q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.M), dtype=torch.float32, device=dev)
-        return q, k, v, o, lse
+        splits = splits_of(w)
+        need = fa2.fa2_fwd_workspace_bytes(w.B, w.H, w.M, w.D, splits)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        return q, k, v, o, lse, ws, splits
 
     def launcher(w, bufs):
-        q, k, v, o, lse = bufs
-        code = {"f32": fa2.FA2_DTYPE_F32, "bf16": fa2.FA2_DTYPE_BF16, "f16": fa2.FA2_DTYPE_F16}[w.dtype]
-        args_ = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                 w.B, w.H, w.M, w.N, w.D, w.scale, int(w.causal), code, stream.cuda_stream)
+        q, k, v, o, lse, ws, splits = bufs
+        code = code_of(w)
+        if w.Hk is None and splits == 1:
+            # the plain entry point
+            args_ = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, w.M, w.N, w.D, w.scale, int(w.causal), code, stream.cuda_stream)
+            call = fa2.fa2_fwd
+        else:
+            args_ = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, w.kv_heads, w.M, w.N, w.D, w.scale, int(w.causal), code, splits,
+                     ws.data_ptr(), ws.numel(), stream.cuda_stream)
+            call = fa2.fa2_fwd_ex
 
         def fn():
-            st = fa2.fa2_fwd(*args_)
+            st = call(*args_)
             if st != fa2.FA2_OK:
                 raise fa2.Fa2Error(st)
         return fn
@@ -284,12 +317,11 @@ def main(argv=None):
     mean_launch_ms = sum(launch_ms) / len(launch_ms)
     value = w.flops / (ms_per_step * 1e-3) / 1e12
 
-    achieved = w.flops / (mean_launch_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
-    roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+    bound, achieved, peak, unit = roofline_of(w, mean_launch_ms * 1e-3)
+    roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name),
                 "mean_launch_us": round(mean_launch_ms * 1e3, 2),
-                "kernel": f"{dominant_kernel(w)} (D={w.D}, causal={int(w.causal)})"}
+                "kernel": f"{dominant_kernel(w, bufs[6])} (D={w.D}, causal={int(w.causal)})"}
 
     ref_us = PAGE_REFERENCE_US.get(w.name)
     vs_baseline = None if ref_us is None else round(value / (w.flops / (ref_us * 1e-6) / 1e12), 3)
@@ -299,9 +331,9 @@ def main(argv=None):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": vs_baseline,
         "dtype": w.dtype, "data": "synthetic (seeded Gaussian Q/K/V)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "M": w.M, "N": w.N, "D": w.D,
-                   "causal": w.causal, "io_dtype": w.dtype, "global_batch": w.B, "seq_len": w.M,
-                   "parallelism": "single GPU"},
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hk": w.kv_heads, "M": w.M, "N": w.N,
+                   "D": w.D, "causal": w.causal, "io_dtype": w.dtype, "kv_splits": bufs[6],
+                   "global_batch": w.B, "seq_len": w.M, "parallelism": "single GPU"},
         "roofline": roofline,
     }
     del bufs
@@ -310,7 +342,7 @@ def main(argv=None):
     if not args.no_extras:
         flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
         table = {}
-        for name in workloads.ORDER:
+        for name in workloads.ORDER + workloads.WIDENED:
             wx = workloads.get(name)
             bx = setup(wx)
             fx = launcher(wx, bx)
@@ -318,11 +350,13 @@ def main(argv=None):
             cold = time_launches(fx, stream, 3, 20, flush=flush_buf.zero_)
             us, us_cold = median(hot) * 1e3, median(cold) * 1e3
             tf = wx.flops / (us * 1e-6) / 1e12
-            table[name] = {"shape": f"B={wx.B},H={wx.H},M={wx.M},N={wx.N},D={wx.D}",
-                           "dtype": wx.dtype, "causal": wx.causal,
+            bound, ach, pk, unit = roofline_of(wx, us * 1e-6)
+            table[name] = {"shape": f"B={wx.B},H={wx.H},Hk={wx.kv_heads},M={wx.M},N={wx.N},D={wx.D}",
+                           "dtype": wx.dtype, "causal": wx.causal, "kv_splits": bx[6],
                            "us_median": round(us, 2), "us_median_l2_flushed": round(us_cold, 2),
                            "tflops": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK_TFLOPS[wx.dtype], 4),
-                           "hbm_gbs_compulsory": round(wx.compulsory_bytes / (us * 1e-6) / 1e9, 1)}
+                           "hbm_gbs_compulsory": round(wx.compulsory_bytes / (us * 1e-6) / 1e9, 1),
+                           "bound": bound, "frac_of_bound": round(ach / pk, 4)}
             del bx, fx
         del flush_buf
         result["workloads"] = table

@@ -90,7 +90,7 @@ def _load():
     lib.fa2_fwd_workspace_bytes.restype = ctypes.c_int64
     lib.fa2_fwd_workspace_bytes.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
     lib.fa2_fwd_num_splits.restype = ctypes.c_int
-    lib.fa2_fwd_num_splits.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int, ctypes.c_int]
+    lib.fa2_fwd_num_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -125,8 +125,8 @@ def fa2_fwd_workspace_bytes(B: int, H: int, M: int, D: int, n_splits: int) -> in
     return int(_lib.fa2_fwd_workspace_bytes(B, H, M, D, n_splits))
 
 
-def fa2_fwd_num_splits(B: int, H: int, M: int, N: int, D: int, causal: int, dtype: int) -> int:
-    return int(_lib.fa2_fwd_num_splits(B, H, M, N, D, causal, dtype))
+def fa2_fwd_num_splits(B: int, H: int, Hk: int, M: int, N: int, D: int, causal: int, dtype: int) -> int:
+    return int(_lib.fa2_fwd_num_splits(B, H, Hk, M, N, D, causal, dtype))
 
 
 def fa2_status_string(status: int) -> str:
@@ -179,7 +179,7 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     elif lse.shape != (B, H, M) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor of shape [B,H,M]")
     code = _dtype_code(q)
-    splits = fa2_fwd_num_splits(B, H, M, N, D, int(bool(causal)), code) if n_splits == 0 else int(n_splits)
+    splits = fa2_fwd_num_splits(B, H, Hk, M, N, D, int(bool(causal)), code) if n_splits == 0 else int(n_splits)
     ws_ptr, ws_size = None, 0
     if splits > 1:
         need = fa2_fwd_workspace_bytes(B, H, M, D, splits)

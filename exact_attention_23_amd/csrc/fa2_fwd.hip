@@ -1264,6 +1264,22 @@ int choose_splits(const Entry& e, int64_t BH, int64_t M, int64_t N) {
     return (int)std::max<int64_t>(1, s);
 }
 
+// The problem as the kernels see it.  Without a causal mask, the G query
+// heads that share a K/V head are consecutive in q, o and lse, so their rows
+// form one contiguous sequence of G*M rows against that K/V head: running
+// them as one head of G*M rows reads each K/V tile once per group instead of
+// once per query head, and fills the query tiles when M is small (decoding).
+// The causal mask depends on the row index within a head, so causal problems
+// keep their heads apart.
+struct KernelShape {
+    int64_t BH, H, G, M;
+};
+KernelShape kernel_shape(int64_t B, int64_t H, int64_t Hk, int64_t M, int causal) {
+    const int64_t G = H > 0 ? H / Hk : 1;
+    if (!causal && G > 1) return {B * Hk, Hk, 1, M * G};
+    return {B * H, H, G, M};
+}
+
 int64_t workspace_bytes(int64_t BH, int64_t M, int64_t D, int n_splits) {
     if (n_splits <= 1) return 0;
     const int64_t rows = (int64_t)n_splits * BH * M;
@@ -1278,12 +1294,15 @@ extern "C" int64_t fa2_fwd_workspace_bytes(int64_t B, int64_t H, int64_t M, int6
     return workspace_bytes(B * H, M, D, n_splits);
 }
 
-extern "C" int fa2_fwd_num_splits(int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, int causal, int dtype) {
-    if (B < 0 || H < 0 || M < 0 || N <= 0) return 1;
+extern "C" int fa2_fwd_num_splits(int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D, int causal,
+                                  int dtype) {
+    if (B < 0 || H < 0 || Hk < 1 || M < 0 || N <= 0) return 1;
+    if (H > 0 && (Hk > H || H % Hk != 0)) return 1;
     if (B > ((int64_t)1 << 31) || H > ((int64_t)1 << 31) || M > ((int64_t)1 << 31)) return 1;
     const Entry* e = find_entry(dtype, D, causal);
     if (!e) return 1;
-    return choose_splits(*e, B * H, M, N);
+    const KernelShape ks = kernel_shape(B, H, Hk, M, causal);
+    return choose_splits(*e, ks.BH, ks.M, N);
 }
 
 extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1311,9 +1330,11 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
     if (B > kMax || H > kMax || M >= kMax || N >= kMax) return FA2_ERR_UNSUPPORTED;
     const int64_t BH = B * H;
     if (M * D >= kMax || N * D >= kMax || BH >= kMax) return FA2_ERR_UNSUPPORTED;
-    const int splits = n_splits == 0 ? choose_splits(*e, BH, M, N) : n_splits;
-    const int64_t n_qt = ceil_div(M, e->block_m);
-    if (n_qt * BH * splits >= kMax) return FA2_ERR_UNSUPPORTED;
+    const KernelShape ks = kernel_shape(B, H, Hk, M, causal);
+    if (ks.M * D >= kMax) return FA2_ERR_UNSUPPORTED;
+    const int splits = n_splits == 0 ? choose_splits(*e, ks.BH, ks.M, N) : n_splits;
+    const int64_t n_qt = ceil_div(ks.M, e->block_m);
+    if (n_qt * ks.BH * splits >= kMax) return FA2_ERR_UNSUPPORTED;
 
     const size_t elt = dtype == FA2_DTYPE_F32 ? 4 : 2;
     const size_t o_bytes = (size_t)BH * M * D * elt;
@@ -1339,8 +1360,8 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
 
     FwdParams prm;
     prm.q = q; prm.k = k; prm.v = v; prm.o = o; prm.lse = lse;
-    prm.BH = (int)BH; prm.H = (int)H; prm.G = (int)(H / Hk);
-    prm.M = (int)M; prm.N = (int)N;
+    prm.BH = (int)ks.BH; prm.H = (int)ks.H; prm.G = (int)ks.G;
+    prm.M = (int)ks.M; prm.N = (int)N;
     prm.n_qt = (int)n_qt;
     prm.c_log2 = scale * 1.44269504088896340736f;  // scale * log2(e)
     const int64_t n_tiles = ceil_div(N, e->block_n);
@@ -1355,7 +1376,7 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     void* args[] = {&prm};
-    hipError_t err = hipLaunchKernel(splits > 1 ? e->kernel_split : e->kernel, dim3((unsigned)(n_qt * BH * splits)),
+    hipError_t err = hipLaunchKernel(splits > 1 ? e->kernel_split : e->kernel, dim3((unsigned)(n_qt * ks.BH * splits)),
                                      dim3(e->threads), args, 0, st);
     if (err == hipSuccess && splits > 1) {
         const MergeEntry* me = nullptr;

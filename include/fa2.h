@@ -108,7 +108,10 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   Hk        key/value heads, 1 <= Hk <= H with H % Hk == 0 (any Hk >= 1 when
  *             H == 0).  k and v are [B, Hk, N, D]; query head h reads K/V head
  *             h / (H / Hk).  Hk == H is multi-head attention (fa2_fwd),
- *             Hk == 1 multi-query attention.
+ *             Hk == 1 multi-query attention.  Without a causal mask the
+ *             H / Hk query heads of a group are processed as one sequence of
+ *             (H / Hk) * M rows (they are consecutive in q, o and lse), so
+ *             each K/V tile is read once per group.
  *   n_splits  0: the library chooses (fa2_fwd_num_splits); 1: one kernel over
  *             the whole key range, no workspace; 2..FA2_MAX_SPLITS: the key
  *             range [0, N) is cut into n_splits ranges of whole K/V tiles,
@@ -144,12 +147,14 @@ int64_t fa2_fwd_workspace_bytes(int64_t B, int64_t H, int64_t M, int64_t D, int 
 
 /*
  * fa2_fwd_num_splits -- the split count fa2_fwd_ex uses for n_splits == 0:
- * 1 when B * H * ceil(M / rows_per_workgroup) already fills about three
+ * 1 when the workgroups of the unsplit grid already fill about three
  * quarters of the GPU's workgroup slots (256 CUs), else enough splits to fill
- * them, keeping at least two K/V tiles per split.  Returns 1 for arguments
- * fa2_fwd_ex would reject.  Pure host computation.
+ * them, keeping at least two K/V tiles per split.  (Without a causal mask the
+ * query heads of one K/V group share their workgroups, see fa2_fwd_ex.)
+ * Returns 1 for arguments fa2_fwd_ex would reject.  Pure host computation.
  */
-int fa2_fwd_num_splits(int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, int causal, int dtype);
+int fa2_fwd_num_splits(int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D, int causal,
+                       int dtype);
 
 /* Static, NUL-terminated description of a fa2_status value. */
 const char* fa2_status_string(int status);

@@ -179,11 +179,15 @@ def test_workspace_bytes():
 def test_num_splits_heuristic():
     bf16 = fa2.FA2_DTYPE_BF16
     # a grid that already fills the GPU is never split
-    assert fa2.fa2_fwd_num_splits(4, 16, 4096, 4096, 128, 1, bf16) == 1
+    assert fa2.fa2_fwd_num_splits(4, 16, 16, 4096, 4096, 128, 1, bf16) == 1
     # decode-like: one query tile per head, many keys
-    s = fa2.fa2_fwd_num_splits(1, 8, 1, 8192, 128, 0, bf16)
+    s = fa2.fa2_fwd_num_splits(1, 8, 8, 1, 8192, 128, 0, bf16)
     assert 1 < s <= fa2.FA2_MAX_SPLITS and s <= (8192 // 64) // 2
     # few keys: at least two K/V tiles per split
-    assert fa2.fa2_fwd_num_splits(1, 1, 1, 128, 128, 0, bf16) == 1
+    assert fa2.fa2_fwd_num_splits(1, 1, 1, 1, 128, 128, 0, bf16) == 1
+    # grouped heads without a causal mask share workgroups: fewer, fuller
+    # workgroups than one per query head
+    assert fa2.fa2_fwd_num_splits(1, 32, 4, 1, 8192, 128, 0, bf16) == fa2.fa2_fwd_num_splits(1, 4, 4, 8, 8192, 128, 0, bf16)
     # arguments the entry point would reject
-    assert fa2.fa2_fwd_num_splits(1, 1, 1, 128, 96, 0, bf16) == 1
+    assert fa2.fa2_fwd_num_splits(1, 1, 1, 1, 128, 96, 0, bf16) == 1
+    assert fa2.fa2_fwd_num_splits(1, 6, 4, 1, 128, 128, 0, bf16) == 1

@@ -78,7 +78,7 @@ def test_split_kv_decode_shapes_auto(M, dtype):
     # few query rows over many keys: the case split K/V exists for
     B, H, N, D = 2, 8, 4096, 128
     code = {"f32": fa2.FA2_DTYPE_F32, "bf16": fa2.FA2_DTYPE_BF16, "f16": fa2.FA2_DTYPE_F16}[dtype]
-    splits = fa2.fa2_fwd_num_splits(B, H, M, N, D, 0, code)
+    splits = fa2.fa2_fwd_num_splits(B, H, 2, M, N, D, 0, code)
     note(f"auto splits for M={M}: {splits}")
     assert splits > 1
     check(B, H, 2, M, N, D, dtype, False, n_splits=0, seed=M)

@@ -69,6 +69,24 @@ def test_workload_parity(name):
     check_case(w.B, w.H, w.M, w.N, w.D, w.dtype, w.causal, w.seed, w.qk_sigma, w.v_sigma, rows=rows)
 
 
+@pytest.mark.parametrize("name", workloads.WIDENED)
+def test_widened_workload_parity(name):
+    # grouped-query heads, fp16 and split K/V at measured sizes
+    import exact_attention_23_amd as fa2
+    w = workloads.get(name)
+    note("case " + w.describe() + f" n_splits={w.n_splits}")
+    q, k, v = workloads.workload_inputs(w)
+    o, lse = fa2.forward(q.cuda(), k.cuda(), v.cuda(), causal=w.causal, n_splits=w.n_splits)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    rows = workloads.sample_rows(w)
+    o_ref, l_ref = oracle.attention(q, k, v, w.scale, w.causal, rows=None if rows is None else rows.numpy())
+    if rows is not None:
+        o, lse = o[:, :, rows.numpy()], lse[:, :, rows.numpy()]
+    compare(o, lse, o_ref, l_ref, w.dtype, name)
+
+
 # ------------------------------------------- the pages' harness shapes, ragged
 
 # (batch, n_queries, n_keys) of the Triton test harness, run at D in {64, 128}

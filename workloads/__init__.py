@@ -25,7 +25,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "torch_dtype"]
+__all__ = ["Workload", "WORKLOADS", "ORDER", "WIDENED", "get", "make_inputs", "torch_dtype"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -43,6 +43,14 @@ class Workload:
     seed: int = 0
     # number of query rows per head checked against the oracle; None = all
     sample_rows: Optional[int] = None
+    # K/V heads (grouped-query attention); None = H
+    Hk: Optional[int] = None
+    # K/V splits the bench asks for (0 = the library's choice, 1 = unsplit)
+    n_splits: int = 1
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hk is None else self.Hk
 
     @property
     def scale(self) -> float:
@@ -67,10 +75,12 @@ class Workload:
     def compulsory_bytes(self) -> int:
         """Read Q, K, V once and write O and the fp32 logsumexp once."""
         bh = self.B * self.H
-        return bh * (2 * self.M * self.D + 2 * self.N * self.D) * self.elt_bytes + 4 * bh * self.M
+        kv = self.B * self.kv_heads * 2 * self.N * self.D
+        return (bh * 2 * self.M * self.D + kv) * self.elt_bytes + 4 * bh * self.M
 
     def describe(self) -> str:
-        return (f"{self.name}: B={self.B},H={self.H},M={self.M},N={self.N},D={self.D},"
+        hk = "" if self.Hk is None else f",Hk={self.Hk}"
+        return (f"{self.name}: B={self.B},H={self.H}{hk},M={self.M},N={self.N},D={self.D},"
                 f"{self.dtype},{'causal' if self.causal else 'non-causal'}")
 
 
@@ -90,6 +100,20 @@ WORKLOADS = {
 }
 
 ORDER = ["tiny_f32", "mha_f32_2k", "causal_bf16_4k", "causal_bf16_16k", "ragged_bf16_cross"]
+
+# The widened rows (grouped-query heads, fp16, split K/V), measured and
+# checked like the workloads above but not part of the headline set.
+WORKLOADS.update({
+    # the causal 4k shape with fp16 inputs
+    "causal_f16_4k": Workload("causal_f16_4k", 4, 16, 4096, 4096, 128, "f16", True, seed=6),
+    # the causal 4k shape with 4 query heads per K/V head
+    "gqa_bf16_4k": Workload("gqa_bf16_4k", 4, 16, 4096, 4096, 128, "bf16", True, seed=7, Hk=4),
+    # decode-like: 16 new query rows per head against a 16k-key cache, 4 query
+    # heads per K/V head, split K/V chosen by the library
+    "decode_gqa_bf16": Workload("decode_gqa_bf16", 4, 32, 16, 16384, 128, "bf16", False, seed=8,
+                                Hk=8, n_splits=0),
+})
+WIDENED = ["causal_f16_4k", "gqa_bf16_4k", "decode_gqa_bf16"]
 
 
 def get(name: str) -> Workload:
@@ -122,7 +146,7 @@ def make_inputs(B: int, H: int, M: int, N: int, D: int, dtype: str = "f32", seed
 
 
 def workload_inputs(w: Workload):
-    return make_inputs(w.B, w.H, w.M, w.N, w.D, w.dtype, w.seed, w.qk_sigma, w.v_sigma)
+    return make_inputs(w.B, w.H, w.M, w.N, w.D, w.dtype, w.seed, w.qk_sigma, w.v_sigma, Hk=w.Hk)
 
 
 def sample_rows(w: Workload, seed_offset: int = 1000):
