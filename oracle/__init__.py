@@ -1,4 +1,4 @@
-"""CPU oracle for the attention forward pass -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the attention forward and backward -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product library never links,
@@ -9,8 +9,9 @@ row at a time, no -ffast-math).  This module only builds that file with gcc
 and marshals arrays into it through ctypes.
 
 Every function of the oracle is pinned by ``tests/test_oracle.py`` to closed
-forms, invariants, a library special case and a 50-digit brute force; none is
-"parity unpinned".
+forms, invariants, a library special case and a 50-digit brute force (the
+backward also to central finite differences of the forward); none is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -50,6 +51,13 @@ def _bind(lib):
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+    ]
+    lib.fa2_oracle_bwd_gqa.restype = ctypes.c_int
+    lib.fa2_oracle_bwd_gqa.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_double, ctypes.c_int, ctypes.c_int,
     ]
     lib.fa2_oracle_max_threads.restype = ctypes.c_int
     lib.fa2_oracle_max_threads.argtypes = []
@@ -127,3 +135,26 @@ def attention(q, k, v, scale: float, causal: bool, rows: Optional[np.ndarray] = 
         raise ValueError(f"fa2_oracle_fwd failed with status {rc}")
     del rows_a
     return o, lse
+
+
+def attention_bwd(q, k, v, dout, scale: float, causal: bool, threads: int = 0, _lib_override=None):
+    """Reference gradients of the attention forward for the upstream gradient
+    dout: q, dout [B,H,M,D]; k, v [B,Hk,N,D].  Returns (dq, dk, dv) as float64
+    numpy arrays shaped like q, k, v; dk and dv sum over the query heads of
+    each K/V head."""
+    qa, ka, va, da = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
+    B, H, M, D = qa.shape
+    Hk, N = ka.shape[1], ka.shape[2]
+    if (ka.shape != (B, Hk, N, D) or va.shape != (B, Hk, N, D) or da.shape != qa.shape
+            or Hk < 1 or H % Hk):
+        raise ValueError(f"shape mismatch q{qa.shape} k{ka.shape} v{va.shape} dout{da.shape}")
+    dq = np.empty((B, H, M, D), dtype=np.float64)
+    dk = np.empty((B, Hk, N, D), dtype=np.float64)
+    dv = np.empty((B, Hk, N, D), dtype=np.float64)
+    lib = _load() if _lib_override is None else _lib_override
+    rc = lib.fa2_oracle_bwd_gqa(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data,
+                                dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                B, H, Hk, M, N, D, float(scale), int(bool(causal)), int(threads))
+    if rc != 0:
+        raise ValueError(f"fa2_oracle_bwd_gqa failed with status {rc}")
+    return dq, dk, dv

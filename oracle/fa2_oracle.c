@@ -1,5 +1,6 @@
 /*
- * fa2_oracle.c -- the CPU reference ("oracle") for the attention forward pass.
+ * fa2_oracle.c -- the CPU reference ("oracle") for the attention forward pass
+ * and its gradients (the backward pass, at the end of this file).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or
  * calls this file: only the test suite, the smoke check and the bench's
@@ -171,4 +172,123 @@ int fa2_oracle_fwd(const float* q, const float* k, const float* v, double* o,
                    int64_t n_rows, int n_threads) {
     return fa2_oracle_fwd_gqa(q, k, v, o, lse, B, H, H > 0 ? H : 1, M, N, D,
                               scale, causal, rows, n_rows, n_threads);
+}
+
+/*
+ * Backward pass (gradients of the forward above with respect to q, k, v for a
+ * given upstream gradient dO), the plain chain rule through the softmax,
+ * evaluated in IEEE double.  For every (b, h) and query row i, with J and
+ * P_ij = e_j / l from steps (1)-(4):
+ *
+ *   dV[j]   += P_ij * dO[i]                               for j in J   (7)
+ *   dP_ij    = <dO[i], V[j]>                                           (8)
+ *   D_i      = sum_{j in J} P_ij * dP_ij                               (9)
+ *   dS_ij    = P_ij * (dP_ij - D_i)                                    (10)
+ *   dQ[i]    = scale * sum_{j in J} dS_ij * K[j]                       (11)
+ *   dK[j]   += scale * dS_ij * Q[i]                                    (12)
+ *
+ * dK and dV of a K/V head sum over every query head that reads it (hk).
+ * Sources: "From FlashAttention to FlashAttention 2", section "Layer 7: The
+ * Backward Kernel" (steps 3-7 of its inner loop: dP = dO V^T, dS = P o (dP -
+ * rowsum(dO o O)), dV += P^T dO, dK += dS^T Q, dQ = dS K) and section
+ * "Backward Pass: Recomputation".  (9) is the definition rowsum(P o dP); it
+ * equals rowsum(dO o O) when O is the exact forward output, the form the
+ * page uses.  The scale enters (11) and (12) because S = scale * Q K^T.
+ * No tiling: one query row at a time, P and dP materialised per row.
+ */
+static void oracle_bwd_row(const float* qi, const float* doi, const float* kbh,
+                           const float* vbh, double* dqi, double* dkbh,
+                           double* dvbh, int64_t i, int64_t N, int64_t D,
+                           double scale, int causal, double* p, double* dp) {
+    const int64_t n_vis = causal ? (i + 1 < N ? i + 1 : N) : N;
+    /* P_ij, steps (1)-(4) of the forward */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n_vis; ++j) {
+        const float* kj = kbh + j * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += (double)qi[d] * (double)kj[d];
+        p[j] = scale * dot;
+        if (p[j] > m) m = p[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < n_vis; ++j) {
+        p[j] = exp(p[j] - m);
+        l += p[j];
+    }
+    for (int64_t j = 0; j < n_vis; ++j) p[j] /= l;
+    /* (8) and (9) */
+    double Di = 0.0;
+    for (int64_t j = 0; j < n_vis; ++j) {
+        const float* vrow = vbh + j * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += (double)doi[d] * (double)vrow[d];
+        dp[j] = dot;
+        Di += p[j] * dot;
+    }
+    /* (7), (10), (11), (12) */
+    for (int64_t d = 0; d < D; ++d) dqi[d] = 0.0;
+    for (int64_t j = 0; j < n_vis; ++j) {
+        const double ds = p[j] * (dp[j] - Di);
+        const float* kj = kbh + j * D;
+        double* dkj = dkbh + j * D;
+        double* dvj = dvbh + j * D;
+        for (int64_t d = 0; d < D; ++d) {
+            dvj[d] += p[j] * (double)doi[d];
+            dqi[d] += scale * ds * (double)kj[d];
+            dkj[d] += scale * ds * (double)qi[d];
+        }
+    }
+}
+
+/*
+ * q, dO: [B,H,M,D]; k, v: [B,Hk,N,D]; outputs dq [B,H,M,D], dk and dv
+ * [B,Hk,N,D] in double.  Work is split over the B*Hk K/V heads (each thread
+ * owns its K/V head's dk, dv), so no two threads add into the same row.
+ * Returns 0 on success.
+ */
+int fa2_oracle_bwd_gqa(const float* q, const float* k, const float* v,
+                       const float* dout, double* dq, double* dk, double* dv,
+                       int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N,
+                       int64_t D, double scale, int causal, int n_threads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return FA2_ORACLE_EINVAL;
+    if (B < 0 || H < 0 || M < 0 || N <= 0 || D <= 0) return FA2_ORACLE_EINVAL;
+    if (Hk < 1 || H % Hk != 0) return FA2_ORACLE_EINVAL;
+    const int64_t group = H / Hk;
+    const int64_t BHk = B * Hk;
+    int status = FA2_ORACLE_OK;
+    for (int64_t x = 0; x < BHk * N * D; ++x) { dk[x] = 0.0; dv[x] = 0.0; }
+#ifdef _OPENMP
+    int nt = n_threads > 0 ? n_threads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+#endif
+    {
+        double* p = (double*)malloc((size_t)N * sizeof(double));
+        double* dp = (double*)malloc((size_t)N * sizeof(double));
+        if (!p || !dp) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            status = FA2_ORACLE_ENOMEM;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t bk = 0; bk < BHk; ++bk) {
+            if (!p || !dp) continue;
+            const int64_t b = bk / Hk, hk = bk % Hk;
+            const float* kbh = k + bk * N * D;
+            const float* vbh = v + bk * N * D;
+            for (int64_t g = 0; g < group; ++g) {
+                const int64_t bh = b * H + hk * group + g; /* (hk) */
+                for (int64_t i = 0; i < M; ++i)
+                    oracle_bwd_row(q + (bh * M + i) * D, dout + (bh * M + i) * D,
+                                   kbh, vbh, dq + (bh * M + i) * D,
+                                   dk + bk * N * D, dv + bk * N * D, i, N, D,
+                                   scale, causal, p, dp);
+            }
+        }
+        free(p);
+        free(dp);
+    }
+    return status;
 }
