@@ -1,15 +1,16 @@
-"""Python binding of libfa2 (exact attention forward pass on gfx950).
+"""Python binding of libfa2 (exact attention forward and backward passes on gfx950).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libfa2.so``.  PyTorch is used for device memory and streams.
 There is no CPU fallback: if the library is missing, importing the binding
 raises.
 
-``fa2_fwd``, ``fa2_fwd_ex``, ``fa2_fwd_workspace_bytes`` and
-``fa2_fwd_num_splits`` mirror the C entry points of ``include/fa2.h`` one to
-one (raw device pointers and sizes).  ``forward`` is the tensor-level
-convenience that allocates ``o``, ``lse`` and any split-K/V workspace with
-torch and calls ``fa2_fwd_ex`` on the current stream.
+``fa2_fwd``, ``fa2_fwd_ex``, ``fa2_fwd_workspace_bytes``,
+``fa2_fwd_num_splits`` and ``fa2_bwd`` mirror the C entry points of
+``include/fa2.h`` one to one (raw device pointers and sizes).  ``forward`` and
+``backward`` are the tensor-level conveniences that allocate outputs (and any
+split-K/V workspace) with torch and call the library on the current stream;
+``attention`` wraps both in a ``torch.autograd.Function``.
 """
 from __future__ import annotations
 
@@ -19,8 +20,8 @@ import os
 
 __all__ = ["FA2_DTYPE_F32", "FA2_DTYPE_BF16", "FA2_DTYPE_F16", "FA2_OK", "FA2_ERR_INVALID_ARGUMENT",
            "FA2_ERR_UNSUPPORTED", "FA2_ERR_LAUNCH", "FA2_ERR_NO_DEVICE", "FA2_MAX_SPLITS", "Fa2Error",
-           "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_workspace_bytes", "fa2_fwd_num_splits",
-           "fa2_status_string", "forward", "library_path", "EXPORTED_SYMBOLS"]
+           "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_workspace_bytes", "fa2_fwd_num_splits", "fa2_bwd",
+           "fa2_status_string", "forward", "backward", "attention", "library_path", "EXPORTED_SYMBOLS"]
 
 FA2_DTYPE_F32 = 0
 FA2_DTYPE_BF16 = 1
@@ -34,7 +35,7 @@ FA2_ERR_NO_DEVICE = 4
 
 FA2_MAX_SPLITS = 128
 
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_ex", "fa2_fwd_num_splits", "fa2_fwd_workspace_bytes",
+EXPORTED_SYMBOLS = ("fa2_bwd", "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_num_splits", "fa2_fwd_workspace_bytes",
                     "fa2_status_string")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +92,9 @@ def _load():
     lib.fa2_fwd_workspace_bytes.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
     lib.fa2_fwd_num_splits.restype = ctypes.c_int
     lib.fa2_fwd_num_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int]
+    lib.fa2_bwd.restype = ctypes.c_int
+    lib.fa2_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -127,6 +131,15 @@ def fa2_fwd_workspace_bytes(B: int, H: int, M: int, D: int, n_splits: int) -> in
 
 def fa2_fwd_num_splits(B: int, H: int, Hk: int, M: int, N: int, D: int, causal: int, dtype: int) -> int:
     return int(_lib.fa2_fwd_num_splits(B, H, Hk, M, N, D, causal, dtype))
+
+
+def fa2_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, delta: int,
+            B: int, H: int, Hk: int, M: int, N: int, D: int, scale: float, causal: int, dtype: int,
+            stream: int | None) -> int:
+    """Direct call of the backward C entry point; pointers are integers.
+    Returns the fa2_status code."""
+    return int(_lib.fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hk, M, N, D, scale, causal,
+                            dtype, stream))
 
 
 def fa2_status_string(status: int) -> str:
@@ -196,3 +209,90 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if st != FA2_OK:
         raise Fa2Error(st)
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, delta=None):
+    """Gradients of the attention forward on the current CUDA/HIP stream.
+
+    q, o, dout: [B,H,M,D]; k, v: [B,Hk,N,D], contiguous device tensors of one
+    dtype (bfloat16 or float16); lse: the forward's [B,H,M] float32 output
+    for the same inputs, scale and causal flag.  Returns (dq, dk, dv), shaped
+    and typed like q, k, v; dk and dv sum over the query heads of each K/V
+    head.  ``delta`` ([B,H,M] float32, rowsum(dout * o)) is scratch the call
+    writes; it is allocated with torch unless given.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D tensor")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, o and dout must share one dtype")
+    B, H, M, D = q.shape
+    Hk, N = k.shape[1], k.shape[2]
+    if (k.shape != (B, Hk, N, D) or v.shape != (B, Hk, N, D) or o.shape != q.shape
+            or dout.shape != q.shape or Hk < 1 or H % Hk):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)} "
+                         f"o{tuple(o.shape)} dout{tuple(dout.shape)}")
+    if (not isinstance(lse, torch.Tensor) or lse.shape != (B, H, M) or lse.dtype != torch.float32
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B,H,M]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+
+    def _out(t, like, name):
+        if t is None:
+            return torch.empty_like(like)
+        if t.shape != like.shape or t.dtype != like.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like its input")
+        return t
+
+    dq, dk, dv = _out(dq, q, "dq"), _out(dk, k, "dk"), _out(dv, v, "dv")
+    if delta is None:
+        delta = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    elif delta.shape != (B, H, M) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 tensor of shape [B,H,M]")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                     B, H, Hk, M, N, D, float(scale), int(bool(causal)), _dtype_code(q), stream)
+    if st != FA2_OK:
+        raise Fa2Error(st)
+    return dq, dk, dv
+
+
+def _make_function():
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale):
+            o, lse = forward(q, k, v, causal=causal, scale=scale)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.causal, ctx.scale = causal, scale
+            return o
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv = backward(q, k, v, o, lse, dout.contiguous(), causal=ctx.causal, scale=ctx.scale)
+            return dq, dk, dv, None, None
+
+    return _Attention
+
+
+_function = None
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None):
+    """softmax(scale * q k^T) v with autograd: the forward runs fa2_fwd_ex,
+    the backward fa2_bwd (bfloat16 / float16 inputs for the backward)."""
+    global _function
+    if _function is None:
+        _function = _make_function()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _function.apply(q, k, v, bool(causal), float(scale))

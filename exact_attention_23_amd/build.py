@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "fa2_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", name) for name in ("fa2_fwd.hip", "fa2_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa2.so")
 ARCH = "gfx950"
@@ -28,7 +28,7 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
            # keep the compiler from forming packed fp32 VALU ops
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", INCLUDE, SRC, "-o", LIB + ".tmp"]
+           "-I", INCLUDE, *SRCS, "-o", LIB + ".tmp"]
     if resource_usage:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     if verbose:

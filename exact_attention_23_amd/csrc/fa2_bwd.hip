@@ -1,0 +1,716 @@
+// fa2_bwd.hip -- gradients of exact attention (the FlashAttention-2 backward
+// schedule) for AMD CDNA4 / gfx950, behind the C ABI declared in include/fa2.h.
+//
+// What is computed, for the forward O = softmax(scale * Q K^T) V (optionally
+// causal) whose per-row logsumexp L the forward pass stored, and an upstream
+// gradient dO:
+//
+//   P     = exp(scale * Q K^T - L)              (recomputed, never stored)
+//   dV    = P^T dO
+//   dP    = dO V^T
+//   Delta = rowsum(dO o O)                      (= rowsum(P o dP))
+//   dS    = P o (dP - Delta)
+//   dQ    = scale * dS K
+//   dK    = scale * dS^T Q
+//
+// with dK, dV summed over the query heads that share a K/V head.  Sources:
+// "From FlashAttention to FlashAttention 2", section "Layer 7: The Backward
+// Kernel" (the recomputation of P from the stored L, the five products and
+// the per-row correction term rowsum(dO o O)) and section "Backward Pass:
+// Recomputation" (why only L is kept from the forward); "FlashAttention-2
+// from PyTorch to Triton", opening section (L is the second output of the
+// forward, stored for the backward).
+//
+// Schedule (our own design for gfx950):
+//  * a small kernel computes Delta per query row (HBM-bound, one pass over
+//    O and dO);
+//  * the dK/dV kernel gives each workgroup one tile of keys (32 per wave) of
+//    one K/V head and streams the query tiles of every query head of its
+//    group through LDS; K and V of the wave's keys stay in VGPRs, dK and dV
+//    accumulate in registers and are written once -- no atomics;
+//  * the dQ kernel gives each workgroup one tile of queries (32 per wave),
+//    keeps Q and dO in VGPRs and streams K/V tiles through LDS, exactly like
+//    the forward; it recomputes P and dP rather than accumulating dQ with
+//    atomics from the dK/dV kernel, so every gradient is written once by one
+//    workgroup and the result is deterministic run to run.
+//
+// MFMA operand mapping (32x32x16, bf16 / fp16; lane l owns accumulator column
+// l % 32).  dK/dV kernel: S = Q K^T and dP = dO V^T take the tile's Q / dO
+// rows as A operands (row reads from LDS) and the wave's K / V rows as B
+// operands (registers), so each lane owns one key and holds 16 of the tile's
+// queries; the P and dS accumulators are then exactly the B operands of
+// dV^T += dO^T P and dK^T += Q^T dS, whose A operands are dO^T / Q^T read
+// with ds_read_b64_tr_b16 in the matching query order.  dQ kernel: the
+// forward's mapping (lane = query): S^T = K Q^T, dP^T = V dO^T, and
+// dQ^T += K^T dS^T with K^T read transposed.  Q and dO tiles (dK/dV kernel)
+// and K tiles (dQ kernel) are read both row-wise and transposed, so they use
+// one XOR swizzle that keeps both patterns free of LDS bank conflicts.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "fa2.h"
+#include "fa2_common.h"
+
+namespace {
+
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* lse;
+    const float* delta;
+    void* dq;
+    void* dk;
+    void* dv;
+    int BH;     // batch * query heads, as the kernels see them
+    int BHk;    // batch * K/V heads
+    int G;      // query heads per K/V head, as the kernels see them (0: none)
+    int M, N;   // query rows per head (kernel view), keys per head
+    int n_qt;   // query tiles per head, of the kernel's own tile height
+    float c_log2;  // scale * log2(e)
+    float scale;
+};
+
+// 16-byte chunk XOR of LDS row r for tiles that are read both row-wise (A
+// operand, 32 rows at one chunk: a quarter-wave covers 16 rows) and
+// transposed (ds_read_b64_tr_b16: a half-wave covers 4 rows x 64 bytes).
+// D = 128 (rows of 256 bytes, one full bank sweep): the low two bits of r
+// pick the 64-byte quarter and bits 2..3 the chunk inside it, so 16
+// consecutive rows hit 16 distinct chunk positions and 4 consecutive rows
+// 4 distinct quarters.  D = 64 (128-byte rows, two per bank sweep): the same
+// with bit 1 in place of bits 0..1 for the half of the row.
+template <int D>
+__device__ __forceinline__ int swz_rt(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+// Per-lane LDS offsets of the two fragment read patterns of a swizzled tile.
+template <int D>
+struct TileReads {
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kDS = D / 16;
+    static constexpr int kDB = D / 32;
+    int row_off[kDS];    // A operand, rows of the 32-row block: lane = row, chunk 2 s + h
+    int tr_lo[kDB];      // A operand of a transposed product, 16-row step: rows 0..7 of the step
+    int tr_hi[kDB];      //   ... rows 8..15
+    __device__ __forceinline__ void init(int lane) {
+        const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int s = 0; s < kDS; ++s) row_off[s] = l32 * kRowBytes + 16 * ((2 * s + h) ^ swz_rt<D>(l32));
+        // ds_read_b64_tr_b16: lane 16 g + 4 t + a addresses row 4 (g >> 1) + t
+        // (+ 8 for the high half) at d = 32 db + 16 (g & 1) + 4 a, and receives
+        // the column d = 32 db + lane % 32 of the four rows its 16-lane group
+        // addressed: slot t of the fragment is row 8 (t >> 2) + 4 (g >> 1) + t % 4
+        // of the step, the order in which a 32x32 accumulator holds rows.
+        const int g = lane >> 4, t = (lane >> 2) & 3, a = lane & 3;
+        const int r_lo = 4 * (g >> 1) + t, r_hi = r_lo + 8;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+            const int c = 4 * db + 2 * (g & 1) + (a >> 1);
+            tr_lo[db] = r_lo * kRowBytes + 16 * (c ^ swz_rt<D>(r_lo)) + 8 * (a & 1);
+            tr_hi[db] = r_hi * kRowBytes + 16 * (c ^ swz_rt<D>(r_hi)) + 8 * (a & 1);
+        }
+    }
+    // A operand of a product over d: rows 32 b .. 32 b + 31, d-step s
+    template <typename V8>
+    __device__ __forceinline__ V8 row(const char* tile, int b, int s) const {
+        return *reinterpret_cast<const V8*>(tile + 32 * b * kRowBytes + row_off[s]);
+    }
+    // A operand of a product over the tile's rows: d block db, rows 16 step ..
+    template <typename V8>
+    __device__ __forceinline__ V8 tr(const char* tile, int step, int db) const {
+        const char* p = tile + 16 * step * kRowBytes;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + tr_lo[db]));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + tr_hi[db]));
+        return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+};
+
+// Byte offsets (inside a tile) of this lane's global -> LDS copies: wave w
+// moves slots [w L 64, (w + 1) L 64); slot s is row s / CPR, physical chunk
+// s % CPR, i.e. logical chunk (s % CPR) ^ swz_rt(row).
+template <int D, int kLoads>
+__device__ __forceinline__ void copy_offsets(uint32_t* off, int wave, int lane) {
+    constexpr int kCPR = D / 8;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int slot = (wave * kLoads + i) * 64 + lane;
+        const int r = slot / kCPR, c = slot % kCPR;
+        off[i] = (uint32_t)(r * 2 * D + 16 * (c ^ swz_rt<D>(r)));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Delta = rowsum(dO o O), fp32
+// ---------------------------------------------------------------------------
+// D / 8 lanes per row, 16 bytes of O and dO each, reduced across the lanes.
+template <typename E, int D>
+__global__ void __launch_bounds__(256)
+fa2_bwd_delta_kernel(const E* __restrict__ O, const E* __restrict__ dO, float* __restrict__ delta, int rows) {
+    using V8 = typename Half<E>::v8;
+    constexpr int kLanes = D / 8;
+    constexpr int kRowsPerWave = 64 / kLanes;
+    const int lane = threadIdx.x & 63;
+    const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave + lane / kLanes;
+    const int c = lane % kLanes;
+    float acc = 0.f;
+    if (row < rows) {
+        const V8 a = *reinterpret_cast<const V8*>(O + (int64_t)row * D + 8 * c);
+        const V8 b = *reinterpret_cast<const V8*>(dO + (int64_t)row * D + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc = fmaf((float)a[i], (float)b[i], acc);
+    }
+#pragma unroll
+    for (int off = kLanes / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && c == 0) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (key tile, K/V head)
+// ---------------------------------------------------------------------------
+// D: head dim; BQ: query rows per streamed tile (32 or 64); NW: waves, each
+// owning 32 consecutive keys.
+template <int D, int BQ, int NW>
+struct BwdKVTraits {
+    static constexpr int kThreads = NW * 64;
+    static constexpr int kBN = 32 * NW;      // keys per workgroup
+    static constexpr int kQB = BQ / 32;      // 32-query blocks per tile
+    static constexpr int kDB = D / 32;
+    static constexpr int kDS = D / 16;
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kTileBytes = BQ * kRowBytes;
+    static constexpr int kLoadsPerWave = BQ * (D / 8) / (64 * NW);
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(BQ == 32 || BQ == 64, "query tile");
+    static_assert(NW >= 2, "waves 0 and 1 stage L and Delta");
+    static_assert(BQ * (D / 8) % (64 * NW) == 0, "loader split");
+};
+
+template <typename E, int D, int BQ, int NW, int WAVES_PER_SIMD, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64, WAVES_PER_SIMD)
+fa2_bwd_dkdv_kernel(const BwdParams p) {
+    using T = BwdKVTraits<D, BQ, NW>;
+    using V8 = typename Half<E>::v8;
+    const E* __restrict__ Q = static_cast<const E*>(p.q);
+    const E* __restrict__ K = static_cast<const E*>(p.k);
+    const E* __restrict__ V = static_cast<const E*>(p.v);
+    const E* __restrict__ dO = static_cast<const E*>(p.dout);
+    E* __restrict__ dK = static_cast<E*>(p.dk);
+    E* __restrict__ dV = static_cast<E*>(p.dv);
+    const int M = p.M, N = p.N;
+    const float c_log2 = p.c_log2;
+    // double-buffered Q and dO tiles, and the tile's L (log2 units) and Delta
+    __shared__ __attribute__((aligned(1024))) char sQ0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sO0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sQ1[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sO1[T::kTileBytes];
+    __shared__ __attribute__((aligned(16))) float sL0[BQ], sL1[BQ], sD0[BQ], sD1[BQ];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+
+    // key tiles major (under a causal mask the first key tile has the most
+    // query tiles), K/V heads fastest
+    const int bkv = blockIdx.x % p.BHk;
+    const int kt = blockIdx.x / p.BHk;
+    const int kbase = kt * T::kBN;
+    const int k0 = kbase + 32 * wave;  // first key of this wave
+    const int key = k0 + l32;          // this lane's key
+
+    // K and V rows of the wave's keys: B operands of S = Q K^T and dP = dO V^T
+    const E* Kh = K + (int64_t)bkv * N * D;
+    const E* Vh = V + (int64_t)bkv * N * D;
+    V8 kf[T::kDS], vf[T::kDS];
+#pragma unroll
+    for (int s = 0; s < T::kDS; ++s) {
+        if (key < N) {
+            kf[s] = *reinterpret_cast<const V8*>(Kh + (int64_t)key * D + 16 * s + 8 * h);
+            vf[s] = *reinterpret_cast<const V8*>(Vh + (int64_t)key * D + 16 * s + 8 * h);
+        } else {
+            kf[s] = V8{};
+            vf[s] = V8{};
+        }
+    }
+
+    // query tiles: every query head of the group, from the first tile that
+    // reaches the workgroup's first key (causal) to the end
+    const int qt0 = CAUSAL ? min(kbase / BQ, p.n_qt) : 0;
+    const int per_g = p.n_qt - qt0;
+    const int n_it = p.G * per_g;
+
+    floatx16 dkacc[T::kDB], dvacc[T::kDB];
+#pragma unroll
+    for (int db = 0; db < T::kDB; ++db) dkacc[db] = dvacc[db] = floatx16{};
+
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t cp_off[T::kLoadsPerWave];
+    copy_offsets<D, T::kLoadsPerWave>(cp_off, wave, lane);
+    TileReads<D> rd;
+    rd.init(lane);
+
+    auto tile_head = [&](int it, int& bh, int& qt) {
+        const int g = it / per_g;
+        qt = qt0 + (it - g * per_g);
+        bh = bkv * p.G + g;
+    };
+    auto issue_tile = [&](int it, char* qdst, char* odst) {
+        int bh, qt;
+        tile_head(it, bh, qt);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BQ>(Q + (int64_t)bh * M * D, cp_off, wave_u, qt, M, qdst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BQ>(dO + (int64_t)bh * M * D, cp_off, wave_u, qt, M, odst);
+    };
+    // wave 0 fetches the tile's L (times log2 e; +inf past M, so those rows
+    // get P = 0), wave 1 its Delta (0 past M)
+    auto fetch_ld = [&](int it) -> float {
+        int bh, qt;
+        tile_head(it, bh, qt);
+        const int row = qt * BQ + lane;
+        if (lane >= BQ || wave > 1) return 0.f;
+        if (wave == 0) return row < M ? p.lse[(int64_t)bh * M + row] * kLog2e : INFINITY;
+        return row < M ? p.delta[(int64_t)bh * M + row] : 0.f;
+    };
+    auto store_ld = [&](float x, float* sl, float* sd) {
+        if (lane < BQ) {
+            if (wave == 0) sl[lane] = x;
+            else if (wave == 1) sd[lane] = x;
+        }
+    };
+
+    auto compute_tile = [&](int it, const char* qs, const char* os, const float* ls, const float* dls) {
+        int bh, qt;
+        tile_head(it, bh, qt);
+        const int row0 = qt * BQ;
+        // nothing to do for keys past N, or (causal) when every query of the
+        // tile precedes every key of the wave
+        if (k0 >= N || (CAUSAL && row0 + BQ - 1 < k0)) return;
+        // S = Q K^T and dP = dO V^T (rows: queries, columns: the wave's keys)
+        floatx16 sacc[T::kQB], pacc[T::kQB];
+#pragma unroll
+        for (int qb = 0; qb < T::kQB; ++qb) sacc[qb] = pacc[qb] = floatx16{};
+#pragma unroll
+        for (int s = 0; s < T::kDS; ++s) {
+            V8 qa[T::kQB], oa[T::kQB];
+#pragma unroll
+            for (int qb = 0; qb < T::kQB; ++qb) {
+                qa[qb] = rd.template row<V8>(qs, qb, s);
+                oa[qb] = rd.template row<V8>(os, qb, s);
+            }
+#pragma unroll
+            for (int qb = 0; qb < T::kQB; ++qb) {
+                sacc[qb] = Half<E>::mfma(qa[qb], kf[s], sacc[qb]);
+                pacc[qb] = Half<E>::mfma(oa[qb], vf[s], pacc[qb]);
+            }
+        }
+        // P = exp2(S c - L2) and dS = P (dP - Delta), rounded once to 16 bits
+        // as B operands of the dV and dK products; register r of the
+        // accumulator holds query row0 + 32 qb + acc_row(r, h).
+        const bool diag = CAUSAL && row0 < k0 + 31;
+        uint32_t pw[T::kQB][2][4], sw[T::kQB][2][4];
+#pragma unroll
+        for (int qb = 0; qb < T::kQB; ++qb) {
+            floatx4 l4[4], d4[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                l4[g] = *reinterpret_cast<const floatx4*>(ls + 32 * qb + 8 * g + 4 * h);
+                d4[g] = *reinterpret_cast<const floatx4*>(dls + 32 * qb + 8 * g + 4 * h);
+            }
+            if (diag) {
+                __asm__ volatile("");  // keep this a branch, not a select per element
+                const int lim = row0 + 32 * qb + 4 * h - key;  // visible iff acc_row part >= -lim
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (8 * (r >> 2) + (r & 3) < -lim) sacc[qb][r] = -INFINITY;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(fmaf(sacc[qb][r], c_log2, -l4[r >> 2][r & 3]));
+                const float p1 = fast_exp2(fmaf(sacc[qb][r + 1], c_log2, -l4[r >> 2][(r & 3) + 1]));
+                const float s0 = p0 * (pacc[qb][r] - d4[r >> 2][r & 3]);
+                const float s1 = p1 * (pacc[qb][r + 1] - d4[r >> 2][(r & 3) + 1]);
+                pw[qb][r >> 3][(r & 7) >> 1] = pack2<E>(p0, p1);
+                sw[qb][r >> 3][(r & 7) >> 1] = pack2<E>(s0, s1);
+            }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over the tile's queries
+#pragma unroll
+        for (int qb = 0; qb < T::kQB; ++qb)
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms) {
+                const V8 pb = __builtin_bit_cast(V8, u32x4{pw[qb][ms][0], pw[qb][ms][1], pw[qb][ms][2], pw[qb][ms][3]});
+                const V8 sb = __builtin_bit_cast(V8, u32x4{sw[qb][ms][0], sw[qb][ms][1], sw[qb][ms][2], sw[qb][ms][3]});
+                V8 oa[T::kDB], qa[T::kDB];
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db) {
+                    oa[db] = rd.template tr<V8>(os, 2 * qb + ms, db);
+                    qa[db] = rd.template tr<V8>(qs, 2 * qb + ms, db);
+                }
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db) {
+                    dvacc[db] = Half<E>::mfma(oa[db], pb, dvacc[db]);
+                    dkacc[db] = Half<E>::mfma(qa[db], sb, dkacc[db]);
+                }
+            }
+    };
+
+    // ---- main loop, unrolled by two over the buffer pair
+    if (n_it > 0) {
+        issue_tile(0, sQ0, sO0);
+        store_ld(fetch_ld(0), sL0, sD0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int it = 0; it < n_it; it += 2) {
+        float nx = 0.f;
+        if (it + 1 < n_it) {
+            issue_tile(it + 1, sQ1, sO1);
+            nx = fetch_ld(it + 1);
+        }
+        compute_tile(it, sQ0, sO0, sL0, sD0);
+        if (it + 1 < n_it) store_ld(nx, sL1, sD1);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
+        __syncthreads();
+        if (it + 1 >= n_it) break;
+        if (it + 2 < n_it) {
+            issue_tile(it + 2, sQ0, sO0);
+            nx = fetch_ld(it + 2);
+        }
+        compute_tile(it + 1, sQ1, sO1, sL1, sD1);
+        if (it + 2 < n_it) store_ld(nx, sL0, sD0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // ---- epilogue: dK = scale dS^T Q, dV = P^T dO, rounded to nearest even
+    if (key < N) {
+        const float scale = p.scale;
+        E* krow = dK + ((int64_t)bkv * N + key) * D;
+        E* vrow = dV + ((int64_t)bkv * N + key) * D;
+#pragma unroll
+        for (int db = 0; db < T::kDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * db + 8 * g + 4 * h;
+                const uint32_t k0w = pack2<E>(dkacc[db][4 * g + 0] * scale, dkacc[db][4 * g + 1] * scale);
+                const uint32_t k1w = pack2<E>(dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale);
+                *reinterpret_cast<uint2*>(krow + d) = make_uint2(k0w, k1w);
+                const uint32_t v0w = pack2<E>(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]);
+                const uint32_t v1w = pack2<E>(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
+                *reinterpret_cast<uint2*>(vrow + d) = make_uint2(v0w, v1w);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (query tile, query head)
+// ---------------------------------------------------------------------------
+// D: head dim; BN: keys per streamed K/V tile (multiple of 32); NW: waves,
+// each owning 32 consecutive query rows.
+template <int D, int BN, int NW>
+struct BwdQTraits {
+    static constexpr int kThreads = NW * 64;
+    static constexpr int kBM = 32 * NW;      // query rows per workgroup
+    static constexpr int kKB = BN / 32;
+    static constexpr int kDB = D / 32;
+    static constexpr int kDS = D / 16;
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kTileBytes = BN * kRowBytes;
+    static constexpr int kLoadsPerWave = BN * (D / 8) / (64 * NW);
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(BN % 32 == 0, "key tile");
+    static_assert(BN * (D / 8) % (64 * NW) == 0, "loader split");
+};
+
+template <typename E, int D, int BN, int NW, int WAVES_PER_SIMD, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64, WAVES_PER_SIMD)
+fa2_bwd_dq_kernel(const BwdParams p) {
+    using T = BwdQTraits<D, BN, NW>;
+    using V8 = typename Half<E>::v8;
+    const E* __restrict__ Q = static_cast<const E*>(p.q);
+    const E* __restrict__ K = static_cast<const E*>(p.k);
+    const E* __restrict__ V = static_cast<const E*>(p.v);
+    const E* __restrict__ dO = static_cast<const E*>(p.dout);
+    E* __restrict__ dQ = static_cast<E*>(p.dq);
+    const int M = p.M, N = p.N;
+    const float c_log2 = p.c_log2;
+    __shared__ __attribute__((aligned(1024))) char sK0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK1[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV1[T::kTileBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+
+    // query tiles major (heaviest first under a causal mask), heads fastest
+    const int bh = blockIdx.x % p.BH;
+    int qt = blockIdx.x / p.BH;
+    if (CAUSAL) qt = p.n_qt - 1 - qt;
+    const int bkv = p.G == 1 ? bh : bh / p.G;
+    const int qw0 = qt * T::kBM + 32 * wave;  // first query row of this wave
+    const int query = qw0 + l32;              // this lane's query row
+
+    // Q and dO rows of the lane's query: B operands of S^T = K Q^T and
+    // dP^T = V dO^T; L (log2 units) and Delta of the row
+    const E* Qh = Q + (int64_t)bh * M * D;
+    const E* dOh = dO + (int64_t)bh * M * D;
+    V8 qf[T::kDS], of[T::kDS];
+#pragma unroll
+    for (int s = 0; s < T::kDS; ++s) {
+        if (query < M) {
+            qf[s] = *reinterpret_cast<const V8*>(Qh + (int64_t)query * D + 16 * s + 8 * h);
+            of[s] = *reinterpret_cast<const V8*>(dOh + (int64_t)query * D + 16 * s + 8 * h);
+        } else {
+            qf[s] = V8{};
+            of[s] = V8{};
+        }
+    }
+    const float l2 = query < M ? p.lse[(int64_t)bh * M + query] * kLog2e : INFINITY;
+    const float dl = query < M ? p.delta[(int64_t)bh * M + query] : 0.f;
+
+    const int kv_end = CAUSAL ? min(N, qt * T::kBM + T::kBM) : N;
+    const int n_kv = (kv_end + BN - 1) / BN;
+    int n_w = 0;  // K/V tiles this wave needs
+    if (qw0 < M) n_w = CAUSAL ? (min(N, qw0 + 32) + BN - 1) / BN : n_kv;
+
+    floatx16 dqacc[T::kDB];
+#pragma unroll
+    for (int db = 0; db < T::kDB; ++db) dqacc[db] = floatx16{};
+
+    const E* Kh = K + (int64_t)bkv * N * D;
+    const E* Vh = V + (int64_t)bkv * N * D;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t cp_off[T::kLoadsPerWave];
+    copy_offsets<D, T::kLoadsPerWave>(cp_off, wave, lane);
+    TileReads<D> rd;
+    rd.init(lane);
+    auto issue_tile = [&](int kt, char* kdst, char* vdst) {
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Kh, cp_off, wave_u, kt, N, kdst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Vh, cp_off, wave_u, kt, N, vdst);
+    };
+
+    auto compute_tile = [&](int kt, const char* ks, const char* vs) {
+        if (kt >= n_w) return;
+        // S^T = K Q^T, dP^T = V dO^T (rows: keys, columns: the wave's queries)
+        floatx16 sacc[T::kKB], pacc[T::kKB];
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb) sacc[kb] = pacc[kb] = floatx16{};
+#pragma unroll
+        for (int s = 0; s < T::kDS; ++s) {
+            V8 ka[T::kKB], va[T::kKB];
+#pragma unroll
+            for (int kb = 0; kb < T::kKB; ++kb) {
+                ka[kb] = rd.template row<V8>(ks, kb, s);
+                va[kb] = rd.template row<V8>(vs, kb, s);
+            }
+#pragma unroll
+            for (int kb = 0; kb < T::kKB; ++kb) {
+                sacc[kb] = Half<E>::mfma(ka[kb], qf[s], sacc[kb]);
+                pacc[kb] = Half<E>::mfma(va[kb], of[s], pacc[kb]);
+            }
+        }
+        // boundary tiles only: keys past N, (causal) keys after the query
+        const int kbase = kt * BN;
+        if (kbase + BN > N || (CAUSAL && kbase + BN - 1 > qw0)) {
+            __asm__ volatile("");
+            int lim = N - 1 - kbase;
+            if (CAUSAL) lim = min(lim, query - kbase);
+            lim -= 4 * h;
+#pragma unroll
+            for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+        }
+        // dS^T = P^T (dP^T - Delta), rounded once: B operand of dQ^T += K^T dS^T
+        uint32_t sw[T::kKB][2][4];
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(fmaf(sacc[kb][r], c_log2, -l2));
+                const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], c_log2, -l2));
+                sw[kb][r >> 3][(r & 7) >> 1] = pack2<E>(p0 * (pacc[kb][r] - dl), p1 * (pacc[kb][r + 1] - dl));
+            }
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms) {
+                const V8 sb = __builtin_bit_cast(V8, u32x4{sw[kb][ms][0], sw[kb][ms][1], sw[kb][ms][2], sw[kb][ms][3]});
+                V8 ka[T::kDB];
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db) ka[db] = rd.template tr<V8>(ks, 2 * kb + ms, db);
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db) dqacc[db] = Half<E>::mfma(ka[db], sb, dqacc[db]);
+            }
+    };
+
+    // ---- main loop, unrolled by two over the buffer pair
+    if (n_kv > 0) issue_tile(0, sK0, sV0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < n_kv; kt += 2) {
+        if (kt + 1 < n_kv) issue_tile(kt + 1, sK1, sV1);
+        compute_tile(kt, sK0, sV0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 >= n_kv) break;
+        if (kt + 2 < n_kv) issue_tile(kt + 2, sK0, sV0);
+        compute_tile(kt + 1, sK1, sV1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // ---- epilogue: dQ = scale dS K, rounded to nearest even
+    if (query < M) {
+        const float scale = p.scale;
+        E* row = dQ + ((int64_t)bh * M + query) * D;
+#pragma unroll
+        for (int db = 0; db < T::kDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * db + 8 * g + 4 * h;
+                const uint32_t w0 = pack2<E>(dqacc[db][4 * g + 0] * scale, dqacc[db][4 * g + 1] * scale);
+                const uint32_t w1 = pack2<E>(dqacc[db][4 * g + 2] * scale, dqacc[db][4 * g + 3] * scale);
+                *reinterpret_cast<uint2*>(row + d) = make_uint2(w0, w1);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side: validation, dispatch table, launches
+// ---------------------------------------------------------------------------
+struct BwdEntry {
+    int dtype, D, causal;
+    const void* delta;
+    const void* dkdv;
+    const void* dq;
+    int kv_threads, kv_block_n, kv_block_q;  // dK/dV kernel: threads, keys per workgroup, query tile
+    int q_threads, q_block_m, q_block_n;     // dQ kernel: threads, queries per workgroup, key tile
+    int delta_rows_per_wg;
+};
+
+#define BWD_KERNEL(...) reinterpret_cast<const void*>(&__VA_ARGS__)
+// D = 64: 4 waves x 32 keys per dK/dV workgroup, 64-row query tiles, two
+// waves per SIMD; D = 128: the dK/dV state (K, V, dK, dV of 32 keys: 192
+// VGPRs per lane) leaves no room for a second wave, so one wave per SIMD.
+#define BWD_ROW(E, code, D, causal, kv_bq, kv_wps, q_bn, q_wps)                                    \
+    {code, D, causal, BWD_KERNEL(fa2_bwd_delta_kernel<E, D>),                                   \
+     BWD_KERNEL(fa2_bwd_dkdv_kernel<E, D, kv_bq, 4, kv_wps, causal>),                            \
+     BWD_KERNEL(fa2_bwd_dq_kernel<E, D, q_bn, 4, q_wps, causal>), 256, 128, kv_bq, 256, 128, q_bn, \
+     4 * (64 / (D / 8))}
+const BwdEntry kBwdTable[] = {
+    BWD_ROW(__bf16, FA2_DTYPE_BF16, 64, false, 64, 2, 64, 2),
+    BWD_ROW(__bf16, FA2_DTYPE_BF16, 64, true, 64, 2, 64, 2),
+    BWD_ROW(__bf16, FA2_DTYPE_BF16, 128, false, 64, 1, 32, 2),
+    BWD_ROW(__bf16, FA2_DTYPE_BF16, 128, true, 64, 1, 32, 2),
+    BWD_ROW(_Float16, FA2_DTYPE_F16, 64, false, 64, 2, 64, 2),
+    BWD_ROW(_Float16, FA2_DTYPE_F16, 64, true, 64, 2, 64, 2),
+    BWD_ROW(_Float16, FA2_DTYPE_F16, 128, false, 64, 1, 32, 2),
+    BWD_ROW(_Float16, FA2_DTYPE_F16, 128, true, 64, 1, 32, 2),
+};
+#undef BWD_ROW
+#undef BWD_KERNEL
+
+const BwdEntry* find_bwd_entry(int dtype, int64_t D, int causal) {
+    for (const BwdEntry& t : kBwdTable)
+        if (t.dtype == dtype && t.D == D && t.causal == causal) return &t;
+    return nullptr;
+}
+
+}  // namespace
+
+extern "C" int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, float* delta,
+                       int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+                       float scale, int causal, int dtype, void* stream) {
+    // ---- argument checks, all before any HIP call
+    if (B < 0 || H < 0 || Hk < 1 || M < 0 || N <= 0 || D <= 0) return FA2_ERR_INVALID_ARGUMENT;
+    // a pointer may be null only when its buffer holds no element
+    const bool q_rows = B > 0 && H > 0 && M > 0, kv_rows = B > 0;
+    if (q_rows && (!q || !o || !lse || !dout || !dq || !delta)) return FA2_ERR_INVALID_ARGUMENT;
+    if (kv_rows && (!k || !v || !dk || !dv)) return FA2_ERR_INVALID_ARGUMENT;
+    if (H > 0 && (Hk > H || H % Hk != 0)) return FA2_ERR_INVALID_ARGUMENT;
+    if (dtype != FA2_DTYPE_F32 && dtype != FA2_DTYPE_BF16 && dtype != FA2_DTYPE_F16) return FA2_ERR_INVALID_ARGUMENT;
+    if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARGUMENT;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA2_ERR_INVALID_ARGUMENT;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+        misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) ||
+        misaligned(lse, 4) || misaligned(delta, 4))
+        return FA2_ERR_INVALID_ARGUMENT;
+
+    const BwdEntry* e = find_bwd_entry(dtype, D, causal);
+    if (!e) return FA2_ERR_UNSUPPORTED;
+
+    const int64_t kMax = (int64_t)1 << 31;
+    if (B > kMax || H > kMax || M >= kMax || N >= kMax) return FA2_ERR_UNSUPPORTED;
+    const int64_t BH = B * H, BHk = B * Hk;
+    if (M * D >= kMax || N * D >= kMax || BH * M >= kMax || BHk >= kMax) return FA2_ERR_UNSUPPORTED;
+    const KernelShape ks = kernel_shape(B, H, Hk, M, causal);
+    // one head's Q, dO (K, V) tiles are copied through a buffer resource whose
+    // byte size is a 32-bit int
+    if (ks.M * D * 2 >= kMax || N * D * 2 >= kMax) return FA2_ERR_UNSUPPORTED;
+    const int64_t n_kt = ceil_div(N, e->kv_block_n);
+    const int64_t n_qt_q = ceil_div(ks.M, e->q_block_m);
+    if (n_kt * BHk >= kMax || n_qt_q * ks.BH >= kMax) return FA2_ERR_UNSUPPORTED;
+
+    // the outputs (dq, dk, dv, delta) overlap no other buffer
+    const size_t elt = 2;
+    const size_t q_bytes = (size_t)BH * M * D * elt;
+    const size_t kv_bytes = (size_t)BHk * N * D * elt;
+    const size_t row_bytes = (size_t)BH * M * 4;
+    const struct {
+        const void* p;
+        size_t n;
+    } bufs[] = {{dq, q_bytes}, {dk, kv_bytes}, {dv, kv_bytes}, {delta, row_bytes}, {q, q_bytes},
+                {k, kv_bytes}, {v, kv_bytes}, {o, q_bytes}, {lse, row_bytes}, {dout, q_bytes}};
+    constexpr int kOutputs = 4;
+    for (int i = 0; i < kOutputs; ++i)
+        for (int j = 0; j < (int)(sizeof(bufs) / sizeof(bufs[0])); ++j)
+            if (j != i && overlaps(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n)) return FA2_ERR_INVALID_ARGUMENT;
+
+    if (BHk == 0) return FA2_OK;  // no K/V rows: nothing to write
+
+    BwdParams prm;
+    prm.q = q; prm.k = k; prm.v = v; prm.dout = dout; prm.lse = lse; prm.delta = delta;
+    prm.dq = dq; prm.dk = dk; prm.dv = dv;
+    prm.BH = (int)ks.BH;
+    prm.BHk = (int)BHk;
+    prm.G = H > 0 ? (int)ks.G : 0;  // no query heads: dK = dV = 0
+    prm.M = (int)ks.M;
+    prm.N = (int)N;
+    prm.c_log2 = scale * kLog2e;
+    prm.scale = scale;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t err = hipSuccess;
+    const int rows = (int)(BH * M);
+    if (rows > 0) {
+        const void* o_arg = o;
+        const void* do_arg = dout;
+        float* d_arg = delta;
+        int r = rows;
+        void* dargs[] = {(void*)&o_arg, (void*)&do_arg, &d_arg, &r};
+        err = hipLaunchKernel(e->delta, dim3((unsigned)ceil_div(rows, e->delta_rows_per_wg)), dim3(256), dargs, 0, st);
+    }
+    if (err == hipSuccess) {
+        prm.n_qt = (int)ceil_div(ks.M, e->kv_block_q);
+        void* args[] = {&prm};
+        err = hipLaunchKernel(e->dkdv, dim3((unsigned)(n_kt * BHk)), dim3(e->kv_threads), args, 0, st);
+    }
+    if (err == hipSuccess && rows > 0) {
+        prm.n_qt = (int)n_qt_q;
+        void* args[] = {&prm};
+        err = hipLaunchKernel(e->dq, dim3((unsigned)(n_qt_q * ks.BH)), dim3(e->q_threads), args, 0, st);
+    }
+    return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}

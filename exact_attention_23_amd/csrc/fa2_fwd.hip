@@ -59,117 +59,9 @@
 #include <algorithm>
 
 #include "fa2.h"
+#include "fa2_common.h"
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
-
-// Buffer resource over `bytes` bytes at `base` (raw, no stride, dword data
-// format): loads past the end return zero instead of touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-
-// Workgroup barrier for LDS hand-offs between waves.  It waits for this
-// wave's own LDS operations only; __syncthreads would also drain every
-// outstanding global->LDS copy (its release fence covers global memory), which
-// forces copies issued for a later tile to land early.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt untouched
-    __asm__ volatile("s_barrier" ::: "memory");
-}
-
-// Copy of one BN-row K or V tile (rows kt*BN ...) of the head at `head` into
-// LDS by buffer loads, 16 bytes per lane per load.  `off` holds this lane's
-// kLoads byte offsets inside a tile
-// (row * row_bytes + swizzled chunk), fixed for the whole kernel; the tile
-// offset is a scalar and the LDS destination of a load is wave-uniform
-// (M0 + 16 * lane), so outside the last tile a copy costs no vector ALU work.
-// Rows past N re-read row N-1 (finite data; their scores are masked).
-template <int kLoads, int kRowBytes, int BN>
-__device__ __forceinline__ void copy_tile_to_lds(const void* head, const uint32_t* off,
-                                                 int wave_u, int kt, int N, char* dst) {
-    // the buffer covers one head's K (V): the range check backs up the clamp
-    const auto rsrc = make_rsrc(head, N * kRowBytes);
-    const int kbase = kt * BN;
-    const int soff = kbase * kRowBytes;
-    char* wdst = dst + wave_u * kLoads * 1024;
-    if (kbase + BN <= N) {
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(wdst + i * 1024),
-                                                     16, off[i], soff, 0, 0);
-    } else {
-        const uint32_t last = (uint32_t)(N - 1 - kbase);
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const uint32_t o = min(off[i] / kRowBytes, last) * kRowBytes + off[i] % kRowBytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(wdst + i * 1024),
-                                                     16, o, soff, 0, 0);
-        }
-    }
-}
-
-// Row of the 32x32 MFMA accumulator held in register r (0..15) by a lane in
-// half h (= lane / 32); the column is lane % 32.
-__device__ __forceinline__ constexpr int acc_row(int r, int h) {
-    return 8 * (r >> 2) + 4 * h + (r & 3);
-}
-
-__device__ __forceinline__ float xchg_half(float x) {
-    // value of the lane in the other 32-lane half (same accumulator column)
-    return __shfl_xor(x, 32, 64);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// The 16-bit input types share every kernel; they differ only in the MFMA
-// opcode, the conversion that rounds P and O (to nearest even in both), and
-// the packed sum of two rounded weights.
-template <typename E>
-struct Half;
-template <>
-struct Half<__bf16> {
-    using v8 = bf16x8;
-    using v2 = bf16x2;
-    static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ float sum2(v2 p, float acc) {  // acc + p.x + p.y
-        const v2 one = {(__bf16)1.0f, (__bf16)1.0f};
-        return __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
-    }
-};
-template <>
-struct Half<_Float16> {
-    using v8 = f16x8;
-    using v2 = f16x2;
-    static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ float sum2(v2 p, float acc) {
-        const v2 one = {(_Float16)1.0f, (_Float16)1.0f};
-        return __builtin_amdgcn_fdot2(p, one, acc, false);
-    }
-};
-
-// Two floats rounded to nearest even and packed (one v_cvt_pk_*_f32).
-template <typename E>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    const typename Half<E>::v2 v = {(E)lo, (E)hi};
-    return __builtin_bit_cast(uint32_t, v);
-}
 
 // ---------------------------------------------------------------------------
 // parameters and work assignment shared by the forward kernels
@@ -298,8 +190,6 @@ __device__ __forceinline__ int swz_v(int r) {
     return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 template <typename E, int D, int BN, int NW, int QB, int WAVES_PER_SIMD, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64, WAVES_PER_SIMD)
@@ -1242,14 +1132,6 @@ const Entry* find_entry(int dtype, int64_t D, int causal) {
     return nullptr;
 }
 
-bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-    return x < y + nb && y < x + na;
-}
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Split count that fills the GPU: 1 when the unsplit grid already occupies
 // three quarters of the workgroup slots; otherwise enough splits to fill them,
@@ -1262,22 +1144,6 @@ int choose_splits(const Entry& e, int64_t BH, int64_t M, int64_t N) {
     s = std::min<int64_t>(s, std::max<int64_t>(1, ceil_div(N, e.block_n) / 2));
     s = std::min<int64_t>(s, FA2_MAX_SPLITS);
     return (int)std::max<int64_t>(1, s);
-}
-
-// The problem as the kernels see it.  Without a causal mask, the G query
-// heads that share a K/V head are consecutive in q, o and lse, so their rows
-// form one contiguous sequence of G*M rows against that K/V head: running
-// them as one head of G*M rows reads each K/V tile once per group instead of
-// once per query head, and fills the query tiles when M is small (decoding).
-// The causal mask depends on the row index within a head, so causal problems
-// keep their heads apart.
-struct KernelShape {
-    int64_t BH, H, G, M;
-};
-KernelShape kernel_shape(int64_t B, int64_t H, int64_t Hk, int64_t M, int causal) {
-    const int64_t G = H > 0 ? H / Hk : 1;
-    if (!causal && G > 1) return {B * Hk, Hk, 1, M * G};
-    return {B * H, H, G, M};
 }
 
 int64_t workspace_bytes(int64_t BH, int64_t M, int64_t D, int n_splits) {
@@ -1310,8 +1176,10 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
                           float scale, int causal, int dtype, int n_splits,
                           void* workspace, int64_t workspace_size, void* stream) {
     // ---- argument checks, all before any HIP call
-    if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARGUMENT;
     if (B < 0 || H < 0 || Hk < 1 || M < 0 || N <= 0 || D <= 0) return FA2_ERR_INVALID_ARGUMENT;
+    // a pointer may be null only when its buffer holds no element
+    const bool q_rows = B > 0 && H > 0 && M > 0, kv_rows = B > 0;
+    if ((q_rows && (!q || !o || !lse)) || (kv_rows && (!k || !v))) return FA2_ERR_INVALID_ARGUMENT;
     if (H > 0 && (Hk > H || H % Hk != 0)) return FA2_ERR_INVALID_ARGUMENT;
     if (dtype != FA2_DTYPE_F32 && dtype != FA2_DTYPE_BF16 && dtype != FA2_DTYPE_F16) return FA2_ERR_INVALID_ARGUMENT;
     if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARGUMENT;
@@ -1332,6 +1200,9 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
     if (M * D >= kMax || N * D >= kMax || BH >= kMax) return FA2_ERR_UNSUPPORTED;
     const KernelShape ks = kernel_shape(B, H, Hk, M, causal);
     if (ks.M * D >= kMax) return FA2_ERR_UNSUPPORTED;
+    // the 16-bit kernels address one head's K (V) through a buffer resource
+    // whose byte size is a 32-bit int
+    if (dtype != FA2_DTYPE_F32 && N * D * 2 >= kMax) return FA2_ERR_UNSUPPORTED;
     const int splits = n_splits == 0 ? choose_splits(*e, ks.BH, ks.M, N) : n_splits;
     const int64_t n_qt = ceil_div(ks.M, e->block_m);
     if (n_qt * ks.BH * splits >= kMax) return FA2_ERR_UNSUPPORTED;

@@ -1,5 +1,5 @@
 /*
- * fa2.h -- C ABI of libfa2: exact attention forward pass for AMD gfx950.
+ * fa2.h -- C ABI of libfa2: exact attention forward and backward passes for AMD gfx950.
  *
  * The operation (all four pages agree on it):
  *
@@ -82,7 +82,9 @@ typedef enum {
  * before libfa2 so both share one runtime: pointers and streams from one HIP
  * runtime are meaningless to another.
  *
- * Alignment: q, k, v, o must be 16-byte aligned, lse 4-byte aligned.
+ * Alignment: q, k, v, o must be 16-byte aligned, lse 4-byte aligned.  A
+ * pointer may be NULL only when its buffer holds no element (q, o, lse when
+ * B*H*M == 0; k, v when B == 0).
  *
  * Errors: all argument checks run before any HIP call; on failure nothing is
  * launched and the outputs are untouched.  M == 0 or B*H == 0 returns FA2_OK
@@ -155,6 +157,53 @@ int64_t fa2_fwd_workspace_bytes(int64_t B, int64_t H, int64_t M, int64_t D, int 
  */
 int fa2_fwd_num_splits(int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D, int causal,
                        int dtype);
+
+/*
+ * fa2_bwd -- gradients of the attention forward pass on one HIP stream.
+ *
+ * For the forward O = softmax(S) V with S = scale * Q K^T (optionally causal,
+ * grouped K/V heads as in fa2_fwd_ex) and an upstream gradient dO, it
+ * computes
+ *   P     = exp(S - L)                     recomputed from the stored lse
+ *   delta = rowsum(dO o O)                 per query row, fp32
+ *   dV    = P^T dO,   dP = dO V^T,   dS = P o (dP - delta)
+ *   dQ    = scale * dS K,   dK = scale * dS^T Q
+ * where dK, dV of a K/V head sum over the H / Hk query heads that read it.
+ * Sources: "From FlashAttention to FlashAttention 2", section "Layer 7: The
+ * Backward Kernel" (recompute P from L; dP, the rowsum(dO o O) correction,
+ * dS and the products for dV, dK, dQ) and section "Backward Pass:
+ * Recomputation"; "FlashAttention-2 from PyTorch to Triton", opening section
+ * (L kept from the forward for the backward).
+ *
+ * Layout: contiguous row-major device arrays.
+ *   q, o, dout, dq  [B, H, M, D]    element type `dtype`
+ *   k, v, dk, dv    [B, Hk, N, D]   element type `dtype`
+ *   lse             [B, H, M]       float32, the forward's logsumexp output
+ *   delta           [B, H, M]       float32 (output): rowsum(dout o o)
+ * o and lse must be the forward's outputs for the same q, k, v, scale and
+ * causal flag.  dq, dk, dv are rounded to nearest even.
+ *
+ * Arguments as for fa2_fwd_ex (B, H, Hk, M, N >= 1, D, scale, causal, dtype,
+ * stream).  This build supports dtype BF16 and F16 with D = 64 or 128; F32
+ * returns FA2_ERR_UNSUPPORTED.
+ *
+ * Ownership: every buffer is caller-allocated device memory; the library
+ * allocates nothing.  The outputs dq, dk, dv and delta must not overlap each
+ * other or any input; q, k, v, o, dout, dq, dk, dv 16-byte aligned, lse and
+ * delta 4-byte aligned.  A pointer may be NULL only when its buffer holds no
+ * element (q, o, lse, dout, dq, delta when B*H*M == 0; k, v, dk, dv when
+ * B == 0).
+ *
+ * Execution: three kernels on `stream` (delta; dK and dV; dQ), no
+ * synchronisation; every output element is written exactly once, by one
+ * workgroup, so results are identical run to run.  M == 0 writes dk = dv = 0;
+ * B * Hk == 0 launches nothing.  Errors as for fa2_fwd: every argument check
+ * runs before any HIP call, and on failure nothing is launched.
+ */
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, float* delta,
+            int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+            float scale, int causal, int dtype, void* stream);
 
 /* Static, NUL-terminated description of a fa2_status value. */
 const char* fa2_status_string(int status);

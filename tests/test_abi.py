@@ -191,3 +191,66 @@ def test_num_splits_heuristic():
     # arguments the entry point would reject
     assert fa2.fa2_fwd_num_splits(1, 1, 1, 1, 128, 96, 0, bf16) == 1
     assert fa2.fa2_fwd_num_splits(1, 6, 4, 1, 128, 128, 0, bf16) == 1
+
+
+def test_bf16_head_addressed_by_32bit_buffer_size():
+    # a 16-bit head of N*D*2 >= 2^31 bytes cannot be described by the kernels'
+    # buffer resource: refused before any launch
+    assert call(N=1 << 23, D=128, dtype=fa2.FA2_DTYPE_BF16) == fa2.FA2_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------ fa2_bwd (no launches)
+
+DO, DQ, DK, DV, DL = 6 * A, 7 * A, 8 * A, 9 * A, 10 * A
+
+
+def call_bwd(q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, delta=DL, B=1, H=2, Hk=2, M=16,
+             N=16, D=64, scale=0.125, causal=0, dtype=None):
+    dtype = fa2.FA2_DTYPE_BF16 if dtype is None else dtype
+    return fa2.fa2_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, Hk, M, N, D, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "delta"])
+def test_bwd_null_pointers_rejected(name):
+    assert call_bwd(**{name: 0}) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(H=-1), dict(Hk=0), dict(H=4, Hk=3), dict(M=-1), dict(N=0),
+                                dict(D=0), dict(scale=0.0), dict(scale=float("nan")), dict(causal=2),
+                                dict(dtype=7)])
+def test_bwd_bad_arguments_rejected(kw):
+    assert call_bwd(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("name,off", [("q", 8), ("dout", 8), ("dq", 2), ("dk", 8), ("dv", 4), ("lse", 2),
+                                      ("delta", 2)])
+def test_bwd_misaligned_pointers_rejected(name, off):
+    base = {"q": Q, "dout": DO, "dq": DQ, "dk": DK, "dv": DV, "lse": L, "delta": DL}[name]
+    kw = {("do" if name == "dout" else name): base + off}
+    assert call_bwd(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_unsupported_dtype_and_head_dim():
+    assert call_bwd(dtype=fa2.FA2_DTYPE_F32) == fa2.FA2_ERR_UNSUPPORTED
+    for D in (32, 96, 256):
+        assert call_bwd(D=D) == fa2.FA2_ERR_UNSUPPORTED
+    assert call_bwd(N=1 << 23, D=128) == fa2.FA2_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(dq=Q), dict(dk=V), dict(dv=DK), dict(delta=DQ + 16), dict(dq=DO),
+                                dict(delta=L), dict(dk=DV + 64)])
+def test_bwd_overlapping_outputs_rejected(kw):
+    assert call_bwd(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_empty_kv_is_a_no_op():
+    # no K/V rows to write: returns before any HIP call
+    assert call_bwd(B=0) == fa2.FA2_OK
+
+
+def test_null_pointers_allowed_for_empty_buffers():
+    # empty q/o/lse (M == 0) may be null; k/v are not empty, so not null
+    assert call(q=0, o=0, lse=0, M=0) == fa2.FA2_OK
+    assert call(k=0, M=0) == fa2.FA2_ERR_INVALID_ARGUMENT
+    assert call_bwd(q=0, o=0, lse=0, do=0, dq=0, delta=0, M=0) != fa2.FA2_ERR_INVALID_ARGUMENT
+    assert call_bwd(dk=0, M=0) == fa2.FA2_ERR_INVALID_ARGUMENT

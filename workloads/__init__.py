@@ -25,7 +25,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "ORDER", "WIDENED", "get", "make_inputs", "torch_dtype"]
+__all__ = ["Workload", "WORKLOADS", "ORDER", "WIDENED", "get", "make_inputs", "make_dout", "torch_dtype"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -163,3 +163,16 @@ def sample_rows(w: Workload, seed_offset: int = 1000):
     inner = torch.randperm(w.M - 2, generator=g)[: w.sample_rows - 2] + 1
     rows = torch.cat([torch.tensor([0, w.M - 1]), inner]).sort().values
     return rows.to(torch.int64)
+
+
+def make_dout(B: int, H: int, M: int, D: int, dtype: str = "bf16", seed: int = 0, sigma: float = 1.0):
+    """Seeded upstream gradient dO [B,H,M,D] for the backward pass: float32
+    standard normals from their own CPU generator (seed + 7919, so dO never
+    repeats the draws of Q), times ``sigma``, rounded to the I/O dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 7919)
+    do = torch.randn((B, H, M, D), generator=g, dtype=torch.float32)
+    if sigma != 1.0:
+        do.mul_(sigma)
+    td = torch_dtype(dtype)
+    return (do.to(td) if td != torch.float32 else do).contiguous()
