@@ -1,6 +1,6 @@
-"""Benchmark of the attention forward pass on one MI355X.
+"""Benchmark of the attention forward (and backward) pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
 
 A step is one fa2_fwd call over one batch of the workload (all of its heads
 and query rows), inputs already resident in HBM.  Before the W counted
@@ -17,7 +17,12 @@ non-causal).  Prints ONE JSON line with the whole-job throughput
   the current kernel source;
 * cpu_baseline: the CPU oracle timed on this host on the same workload;
 * workloads: per-launch latency (median of 100 after 25 warm-ups, with and
-  without an L2/MALL flush before each launch) of every workload.
+  without an L2/MALL flush before each launch) of every workload;
+* backward: per-call latency of fa2_bwd (delta, dK/dV and dQ kernels) on the
+  16-bit workloads, counted as 10*B*H*M*N*D flop (halved for causal).
+
+With --pass bwd the timed step is one fa2_bwd call instead (the forward's o
+and lse are computed once beforehand), counted the same way.
 """
 from __future__ import annotations
 
@@ -34,6 +39,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("attention fwd TFLOP/s (4·B·H·M·N·D) and % of MFMA peak; "
           "latency µs, 1 MI355X")
+METRIC_BWD = ("attention bwd TFLOP/s (10·B·H·M·N·D) and % of MFMA peak; "
+              "latency µs, 1 MI355X")
 # MI355X dense matrix peaks (AMD's published figures): bf16 2.5 PFLOP/s
 # (256 CU x 2.4 GHz x 4096 flop/clk), fp32 157.3 TFLOP/s.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
@@ -42,15 +49,19 @@ HBM_PEAK_GBS = 8000.0
 # at B=4,H=12,M=N=2048,D=64 took 3810.30 us, i.e. 13.53 TFLOP/s by this count.
 PAGE_REFERENCE_US = {"mha_f32_2k": 3810.30}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "exact_attention_23_amd", "csrc", "fa2_fwd.hip")
+# the forward kernels and the helpers they include
+KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", name)
+               for name in ("fa2_fwd.hip", "fa2_common.h")]
 
 
 def kernel_source_hash() -> str:
-    """sha256 of the kernel source with comments and blank space removed, so
-    that counters stay attached to the code they were taken on."""
+    """sha256 of the forward kernel sources with comments and blank space
+    removed, so that counters stay attached to the code they were taken on."""
     import re
-    with open(KERNEL_SRC) as f:
-        src = f.read()
+    src = ""
+    for path in KERNEL_SRCS:
+        with open(path) as f:
+            src += f.read() + "\n"
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     src = "\n".join(" ".join(line.split()) for line in src.splitlines() if line.strip())
@@ -220,6 +231,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="mha_f32_2k")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward pass (fa2_bwd, 16-bit workloads)")
     ap.add_argument("--prewarm", type=float, default=0.3,
                     help="seconds of back-to-back untimed steps before the warm-up steps (clock settling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -290,9 +303,39 @@ def main(argv=None):
                 raise fa2.Fa2Error(st)
         return fn
 
+    def bwd_setup(w):
+        q, k, v, o, lse, ws, splits = setup(w)
+        launcher(w, (q, k, v, o, lse, ws, splits))()  # the forward's o and lse
+        do = workloads.make_dout(w.B, w.H, w.M, w.D, w.dtype, w.seed).to(dev)
+        delta = torch.empty((w.B, w.H, w.M), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        del ws
+        return q, k, v, o, lse, do, torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), delta
+
+    def bwd_launcher(w, b):
+        args_ = tuple(t.data_ptr() for t in b) + (w.B, w.H, w.kv_heads, w.M, w.N, w.D, w.scale,
+                                                   int(w.causal), code_of(w), stream.cuda_stream)
+
+        def fn():
+            st = fa2.fa2_bwd(*args_)
+            if st != fa2.FA2_OK:
+                raise fa2.Fa2Error(st)
+        return fn
+
     w = workloads.get(args.workload)
-    bufs = setup(w)
-    fn = launcher(w, bufs)
+    backward = args.which == "bwd"
+    if backward and w.dtype == "f32":
+        print(json.dumps({"error": "the backward pass has 16-bit kernels only; pick a bf16/f16 workload"}),
+              flush=True)
+        return 2
+    if backward:
+        bufs = bwd_setup(w)
+        fn = bwd_launcher(w, bufs)
+        step_flops = w.bwd_flops
+    else:
+        bufs = setup(w)
+        fn = launcher(w, bufs)
+        step_flops = w.flops
 
     # ---- the timed steps: W untimed, then exactly K, synchronised on both sides
     # (preceded by --prewarm seconds of untimed steps that let the clock settle)
@@ -315,24 +358,37 @@ def main(argv=None):
     launch_ms = [s.elapsed_time(e) for s, e in events]
     ms_per_step = wall * 1e3 / args.steps
     mean_launch_ms = sum(launch_ms) / len(launch_ms)
-    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
 
-    bound, achieved, peak, unit = roofline_of(w, mean_launch_ms * 1e-3)
-    roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name),
-                "mean_launch_us": round(mean_launch_ms * 1e3, 2),
-                "kernel": f"{dominant_kernel(w, bufs[6])} (D={w.D}, causal={int(w.causal)})"}
+    if backward:
+        # one fa2_bwd call: delta, dK/dV and dQ kernels on one stream
+        peak = PEAK_TFLOPS[w.dtype]
+        achieved = step_flops / (mean_launch_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": None,
+                    "mean_launch_us": round(mean_launch_ms * 1e3, 2),
+                    "kernel": f"fa2_bwd: fa2_bwd_delta_kernel + fa2_bwd_dkdv_kernel + fa2_bwd_dq_kernel "
+                              f"(D={w.D}, causal={int(w.causal)})"}
+        splits = 1
+    else:
+        bound, achieved, peak, unit = roofline_of(w, mean_launch_ms * 1e-3)
+        roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                    "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name),
+                    "mean_launch_us": round(mean_launch_ms * 1e3, 2),
+                    "kernel": f"{dominant_kernel(w, bufs[6])} (D={w.D}, causal={int(w.causal)})"}
+        splits = bufs[6]
 
-    ref_us = PAGE_REFERENCE_US.get(w.name)
+    ref_us = None if backward else PAGE_REFERENCE_US.get(w.name)
     vs_baseline = None if ref_us is None else round(value / (w.flops / (ref_us * 1e-6) / 1e12), 3)
 
     result = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC_BWD if backward else METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": vs_baseline,
         "dtype": w.dtype, "data": "synthetic (seeded Gaussian Q/K/V)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hk": w.kv_heads, "M": w.M, "N": w.N,
-                   "D": w.D, "causal": w.causal, "io_dtype": w.dtype, "kv_splits": bufs[6],
+                   "D": w.D, "causal": w.causal, "io_dtype": w.dtype, "kv_splits": splits,
+                   "pass": args.which,
                    "global_batch": w.B, "seq_len": w.M, "parallelism": "single GPU"},
         "roofline": roofline,
     }
@@ -358,10 +414,26 @@ def main(argv=None):
                            "hbm_gbs_compulsory": round(wx.compulsory_bytes / (us * 1e-6) / 1e9, 1),
                            "bound": bound, "frac_of_bound": round(ach / pk, 4)}
             del bx, fx
-        del flush_buf
         result["workloads"] = table
+        # backward passes (one fa2_bwd call each: delta, dK/dV, dQ kernels)
+        btable = {}
+        for name in workloads.BACKWARD:
+            wx = workloads.get(name)
+            bx = bwd_setup(wx)
+            fx = bwd_launcher(wx, bx)
+            hot = time_launches(fx, stream, 10, 50, prewarm_s=args.prewarm)
+            cold = time_launches(fx, stream, 3, 10, flush=flush_buf.zero_)
+            us, us_cold = median(hot) * 1e3, median(cold) * 1e3
+            tf = wx.bwd_flops / (us * 1e-6) / 1e12
+            btable[name] = {"shape": f"B={wx.B},H={wx.H},Hk={wx.kv_heads},M={wx.M},N={wx.N},D={wx.D}",
+                            "dtype": wx.dtype, "causal": wx.causal, "us_median": round(us, 2),
+                            "us_median_l2_flushed": round(us_cold, 2), "tflops": round(tf, 2),
+                            "frac_of_mfma_peak": round(tf / PEAK_TFLOPS[wx.dtype], 4), "bound": "mfma"}
+            del bx, fx
+        del flush_buf
+        result["backward"] = btable
 
-    if not args.no_cpu:
+    if not args.no_cpu and not backward:
         result["cpu_baseline"] = cpu_baseline(w)
 
     print(json.dumps(result), flush=True)

@@ -409,6 +409,250 @@ fa2_bwd_dkdv_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV with wave pairs: one workgroup of 8 waves per (128-key tile, K/V head)
+// ---------------------------------------------------------------------------
+// At D = 128 a wave that keeps its keys' K and V in VGPRs next to the dK and
+// dV accumulators (192 VGPRs) leaves no room for a second wave on its SIMD,
+// and a lone wave cannot overlap its own MFMA and VALU work.  Here the
+// workgroup's K and V stay in LDS instead (read as B operands each tile), and
+// waves w and w + 4 -- which share a SIMD -- own the same 32 keys and split
+// each 64-row query tile: wave w takes rows 0..31, wave w + 4 rows 32..63.
+// Each holds partial dK, dV of its keys; the pair's partials are summed
+// through LDS once at the end.  Two waves per SIMD let one wave's MFMAs run
+// while the other waits on LDS or works through its softmax-gradient VALU
+// block.
+template <int D>
+struct BwdPairTraits {
+    static constexpr int kNW = 8;
+    static constexpr int kThreads = kNW * 64;
+    static constexpr int kBN = 128;            // keys per workgroup
+    static constexpr int kBQ = 64;             // query rows per streamed tile
+    static constexpr int kDB = D / 32;
+    static constexpr int kDS = D / 16;
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kQTileBytes = kBQ * kRowBytes;
+    static constexpr int kKTileBytes = kBN * kRowBytes;
+    static constexpr int kQLoads = kBQ * (D / 8) / (64 * kNW);
+    static constexpr int kKLoads = kBN * (D / 8) / (64 * kNW);
+    static constexpr int kPartBytes = 64 * kDB * 16 * 4;  // one wave's fp32 accumulator set
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(kQLoads >= 1 && kKLoads >= 1, "loader split");
+    // the pair sum puts dK partials over the four Q/dO buffers and dV
+    // partials over the K/V tiles
+    static_assert(kPartBytes <= kQTileBytes && 2 * kPartBytes <= kKTileBytes, "pair sum space");
+};
+
+template <typename E, int D, bool CAUSAL>
+__global__ void __launch_bounds__(512, 2)
+fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
+    using T = BwdPairTraits<D>;
+    using V8 = typename Half<E>::v8;
+    const E* __restrict__ Q = static_cast<const E*>(p.q);
+    const E* __restrict__ K = static_cast<const E*>(p.k);
+    const E* __restrict__ V = static_cast<const E*>(p.v);
+    const E* __restrict__ dO = static_cast<const E*>(p.dout);
+    E* __restrict__ dK = static_cast<E*>(p.dk);
+    E* __restrict__ dV = static_cast<E*>(p.dv);
+    const int M = p.M, N = p.N;
+    const float c_log2 = p.c_log2;
+    __shared__ __attribute__((aligned(1024))) char sK[T::kKTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV[T::kKTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sQ0[T::kQTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sO0[T::kQTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sQ1[T::kQTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sO1[T::kQTileBytes];
+    __shared__ __attribute__((aligned(16))) float sL0[T::kBQ], sL1[T::kBQ], sD0[T::kBQ], sD1[T::kBQ];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int kb = wave & 3;   // the wave's 32-key block of the workgroup's keys
+    const int qb = wave >> 2;  // the wave's 32-row block of each query tile
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+
+    // key tiles major (under a causal mask the first key tile has the most
+    // query tiles), K/V heads fastest
+    const int bkv = blockIdx.x % p.BHk;
+    const int kt = blockIdx.x / p.BHk;
+    const int kbase = kt * T::kBN;
+    const int k0 = kbase + 32 * kb;  // first key of this wave
+    const int key = k0 + l32;        // this lane's key
+
+    const int qt0 = CAUSAL ? min(kbase / T::kBQ, p.n_qt) : 0;
+    const int per_g = p.n_qt - qt0;
+    const int n_it = p.G * per_g;
+
+    floatx16 dkacc[T::kDB], dvacc[T::kDB];
+#pragma unroll
+    for (int db = 0; db < T::kDB; ++db) dkacc[db] = dvacc[db] = floatx16{};
+
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t q_off[T::kQLoads], k_off[T::kKLoads];
+    copy_offsets<D, T::kQLoads>(q_off, wave, lane);
+    copy_offsets<D, T::kKLoads>(k_off, wave, lane);
+    TileReads<D> rd;
+    rd.init(lane);
+    const char* kq = sK + 32 * kb * T::kRowBytes;  // this wave's key rows (B operands)
+    const char* vq = sV + 32 * kb * T::kRowBytes;
+
+    auto tile_head = [&](int it, int& bh, int& qt) {
+        const int g = it / per_g;
+        qt = qt0 + (it - g * per_g);
+        bh = bkv * p.G + g;
+    };
+    auto issue_tile = [&](int it, char* qdst, char* odst) {
+        int bh, qt;
+        tile_head(it, bh, qt);
+        copy_tile_to_lds<T::kQLoads, T::kRowBytes, T::kBQ>(Q + (int64_t)bh * M * D, q_off, wave_u, qt, M, qdst);
+        copy_tile_to_lds<T::kQLoads, T::kRowBytes, T::kBQ>(dO + (int64_t)bh * M * D, q_off, wave_u, qt, M, odst);
+    };
+    // wave 0 fetches the tile's L (times log2 e; +inf past M, so those rows
+    // get P = 0), wave 1 its Delta (0 past M)
+    auto fetch_ld = [&](int it) -> float {
+        int bh, qt;
+        tile_head(it, bh, qt);
+        const int row = qt * T::kBQ + lane;
+        if (wave > 1) return 0.f;
+        if (wave == 0) return row < M ? p.lse[(int64_t)bh * M + row] * kLog2e : INFINITY;
+        return row < M ? p.delta[(int64_t)bh * M + row] : 0.f;
+    };
+    auto store_ld = [&](float x, float* sl, float* sd) {
+        if (wave == 0) sl[lane] = x;
+        else if (wave == 1) sd[lane] = x;
+    };
+
+    auto compute_tile = [&](int it, const char* qs, const char* os, const float* ls, const float* dls) {
+        int bh, qt;
+        tile_head(it, bh, qt);
+        const int r0 = qt * T::kBQ + 32 * qb;  // first query row of the wave's block
+        // nothing to do for keys past N, rows past M, or (causal) when every
+        // row of the block precedes every key of the wave
+        if (k0 >= N || r0 >= M || (CAUSAL && r0 + 31 < k0)) return;
+        // S = Q K^T and dP = dO V^T (rows: the block's queries, columns: the
+        // wave's keys), K and V rows read from LDS as B operands
+        floatx16 sacc = floatx16{}, pacc = floatx16{};
+#pragma unroll
+        for (int s = 0; s < T::kDS; ++s) {
+            const V8 qa = rd.template row<V8>(qs, qb, s);
+            const V8 oa = rd.template row<V8>(os, qb, s);
+            const V8 kf = rd.template row<V8>(kq, 0, s);
+            const V8 vf = rd.template row<V8>(vq, 0, s);
+            sacc = Half<E>::mfma(qa, kf, sacc);
+            pacc = Half<E>::mfma(oa, vf, pacc);
+        }
+        // P = exp2(S c - L2), dS = P (dP - Delta); register r holds query
+        // r0 + acc_row(r, h)
+        if (CAUSAL && r0 < k0 + 31) {
+            __asm__ volatile("");  // keep this a branch, not a select per element
+            const int lim = r0 + 4 * h - key;  // visible iff the acc_row part >= -lim
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) < -lim) sacc[r] = -INFINITY;
+        }
+        uint32_t pw[2][4], sw[2][4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const floatx4 l4 = *reinterpret_cast<const floatx4*>(ls + 32 * qb + 8 * g + 4 * h);
+            const floatx4 d4 = *reinterpret_cast<const floatx4*>(dls + 32 * qb + 8 * g + 4 * h);
+#pragma unroll
+            for (int u = 0; u < 4; u += 2) {
+                const int r = 4 * g + u;
+                const float p0 = fast_exp2(fmaf(sacc[r], c_log2, -l4[u]));
+                const float p1 = fast_exp2(fmaf(sacc[r + 1], c_log2, -l4[u + 1]));
+                pw[r >> 3][(r & 7) >> 1] = pack2<E>(p0, p1);
+                sw[r >> 3][(r & 7) >> 1] = pack2<E>(p0 * (pacc[r] - d4[u]), p1 * (pacc[r + 1] - d4[u + 1]));
+            }
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS over the block's 32 rows
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+            const V8 pb = __builtin_bit_cast(V8, u32x4{pw[ms][0], pw[ms][1], pw[ms][2], pw[ms][3]});
+            const V8 sb = __builtin_bit_cast(V8, u32x4{sw[ms][0], sw[ms][1], sw[ms][2], sw[ms][3]});
+#pragma unroll
+            for (int db = 0; db < T::kDB; ++db) {
+                const V8 oa = rd.template tr<V8>(os, 2 * qb + ms, db);
+                const V8 qa = rd.template tr<V8>(qs, 2 * qb + ms, db);
+                dvacc[db] = Half<E>::mfma(oa, pb, dvacc[db]);
+                dkacc[db] = Half<E>::mfma(qa, sb, dkacc[db]);
+            }
+        }
+    };
+
+    // ---- prologue: the workgroup's K and V tiles, the first Q/dO tile
+    if (n_it > 0) {
+        copy_tile_to_lds<T::kKLoads, T::kRowBytes, T::kBN>(K + (int64_t)bkv * N * D, k_off, wave_u, kt, N, sK);
+        copy_tile_to_lds<T::kKLoads, T::kRowBytes, T::kBN>(V + (int64_t)bkv * N * D, k_off, wave_u, kt, N, sV);
+        issue_tile(0, sQ0, sO0);
+        store_ld(fetch_ld(0), sL0, sD0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // ---- main loop, unrolled by two over the Q/dO buffer pair
+    for (int it = 0; it < n_it; it += 2) {
+        float nx = 0.f;
+        if (it + 1 < n_it) {
+            issue_tile(it + 1, sQ1, sO1);
+            nx = fetch_ld(it + 1);
+        }
+        compute_tile(it, sQ0, sO0, sL0, sD0);
+        if (it + 1 < n_it) store_ld(nx, sL1, sD1);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
+        __syncthreads();
+        if (it + 1 >= n_it) break;
+        if (it + 2 < n_it) {
+            issue_tile(it + 2, sQ0, sO0);
+            nx = fetch_ld(it + 2);
+        }
+        compute_tile(it + 1, sQ1, sO1, sL1, sD1);
+        if (it + 2 < n_it) store_ld(nx, sL0, sD0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // ---- pair sum through LDS: waves 4..7 hand their partials to waves 0..3
+    // (dK partials over the Q/dO buffers, dV partials over the K/V tiles; the
+    // loop's last barrier has retired every read of them)
+    char* const kpart = kb == 0 ? sQ0 : kb == 1 ? sO0 : kb == 2 ? sQ1 : sO1;
+    char* const vpart = (kb < 2 ? sK : sV) + (kb & 1) * T::kPartBytes;
+    if (qb == 1) {
+#pragma unroll
+        for (int db = 0; db < T::kDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int off = ((db * 4 + g) * 64 + lane) * 16;
+                *reinterpret_cast<floatx4*>(kpart + off) =
+                    floatx4{dkacc[db][4 * g], dkacc[db][4 * g + 1], dkacc[db][4 * g + 2], dkacc[db][4 * g + 3]};
+                *reinterpret_cast<floatx4*>(vpart + off) =
+                    floatx4{dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]};
+            }
+    }
+    __syncthreads();
+    // ---- epilogue (waves 0..3): dK = scale dS^T Q, dV = P^T dO, rounded to
+    // nearest even
+    if (qb == 0 && key < N) {
+        const float scale = p.scale;
+        E* krow = dK + ((int64_t)bkv * N + key) * D;
+        E* vrow = dV + ((int64_t)bkv * N + key) * D;
+#pragma unroll
+        for (int db = 0; db < T::kDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int off = ((db * 4 + g) * 64 + lane) * 16;
+                const floatx4 pk = *reinterpret_cast<const floatx4*>(kpart + off);
+                const floatx4 pv = *reinterpret_cast<const floatx4*>(vpart + off);
+                const int d = 32 * db + 8 * g + 4 * h;
+                const uint32_t k0w = pack2<E>((dkacc[db][4 * g + 0] + pk[0]) * scale, (dkacc[db][4 * g + 1] + pk[1]) * scale);
+                const uint32_t k1w = pack2<E>((dkacc[db][4 * g + 2] + pk[2]) * scale, (dkacc[db][4 * g + 3] + pk[3]) * scale);
+                *reinterpret_cast<uint2*>(krow + d) = make_uint2(k0w, k1w);
+                const uint32_t v0w = pack2<E>(dvacc[db][4 * g + 0] + pv[0], dvacc[db][4 * g + 1] + pv[1]);
+                const uint32_t v1w = pack2<E>(dvacc[db][4 * g + 2] + pv[2], dvacc[db][4 * g + 3] + pv[3]);
+                *reinterpret_cast<uint2*>(vrow + d) = make_uint2(v0w, v1w);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dQ: one workgroup per (query tile, query head)
 // ---------------------------------------------------------------------------
 // D: head dim; BN: keys per streamed K/V tile (multiple of 32); NW: waves,
@@ -600,25 +844,27 @@ struct BwdEntry {
 };
 
 #define BWD_KERNEL(...) reinterpret_cast<const void*>(&__VA_ARGS__)
-// D = 64: 4 waves x 32 keys per dK/dV workgroup, 64-row query tiles, two
-// waves per SIMD; D = 128: the dK/dV state (K, V, dK, dV of 32 keys: 192
-// VGPRs per lane) leaves no room for a second wave, so one wave per SIMD.
-#define BWD_ROW(E, code, D, causal, kv_bq, kv_wps, q_bn, q_wps)                                    \
-    {code, D, causal, BWD_KERNEL(fa2_bwd_delta_kernel<E, D>),                                   \
-     BWD_KERNEL(fa2_bwd_dkdv_kernel<E, D, kv_bq, 4, kv_wps, causal>),                            \
-     BWD_KERNEL(fa2_bwd_dq_kernel<E, D, q_bn, 4, q_wps, causal>), 256, 128, kv_bq, 256, 128, q_bn, \
-     4 * (64 / (D / 8))}
+// D = 64: 4 waves x 32 keys per dK/dV workgroup with K and V in VGPRs, 64-row
+// query tiles, two waves per SIMD (measured ~13% faster than the wave-pair
+// kernel at this head dim).  D = 128: the wave-pair kernel (K and V in LDS, 8
+// waves per 128 keys), since K, V, dK and dV of 32 keys in VGPRs would leave
+// room for only one wave per SIMD.
+#define BWD_ROW64(E, code, causal)                                                                 \
+    {code, 64, causal, BWD_KERNEL(fa2_bwd_delta_kernel<E, 64>),                                  \
+     BWD_KERNEL(fa2_bwd_dkdv_kernel<E, 64, 64, 4, 2, causal>),                                   \
+     BWD_KERNEL(fa2_bwd_dq_kernel<E, 64, 64, 4, 2, causal>), 256, 128, 64, 256, 128, 64, 4 * 8}
+#define BWD_ROW128(E, code, causal)                                                                \
+    {code, 128, causal, BWD_KERNEL(fa2_bwd_delta_kernel<E, 128>),                                \
+     BWD_KERNEL(fa2_bwd_dkdv_pair_kernel<E, 128, causal>),                                       \
+     BWD_KERNEL(fa2_bwd_dq_kernel<E, 128, 32, 4, 2, causal>), 512, 128, 64, 256, 128, 32, 4 * 4}
 const BwdEntry kBwdTable[] = {
-    BWD_ROW(__bf16, FA2_DTYPE_BF16, 64, false, 64, 2, 64, 2),
-    BWD_ROW(__bf16, FA2_DTYPE_BF16, 64, true, 64, 2, 64, 2),
-    BWD_ROW(__bf16, FA2_DTYPE_BF16, 128, false, 64, 1, 32, 2),
-    BWD_ROW(__bf16, FA2_DTYPE_BF16, 128, true, 64, 1, 32, 2),
-    BWD_ROW(_Float16, FA2_DTYPE_F16, 64, false, 64, 2, 64, 2),
-    BWD_ROW(_Float16, FA2_DTYPE_F16, 64, true, 64, 2, 64, 2),
-    BWD_ROW(_Float16, FA2_DTYPE_F16, 128, false, 64, 1, 32, 2),
-    BWD_ROW(_Float16, FA2_DTYPE_F16, 128, true, 64, 1, 32, 2),
+    BWD_ROW64(__bf16, FA2_DTYPE_BF16, false),   BWD_ROW64(__bf16, FA2_DTYPE_BF16, true),
+    BWD_ROW128(__bf16, FA2_DTYPE_BF16, false),  BWD_ROW128(__bf16, FA2_DTYPE_BF16, true),
+    BWD_ROW64(_Float16, FA2_DTYPE_F16, false),  BWD_ROW64(_Float16, FA2_DTYPE_F16, true),
+    BWD_ROW128(_Float16, FA2_DTYPE_F16, false), BWD_ROW128(_Float16, FA2_DTYPE_F16, true),
 };
-#undef BWD_ROW
+#undef BWD_ROW64
+#undef BWD_ROW128
 #undef BWD_KERNEL
 
 const BwdEntry* find_bwd_entry(int dtype, int64_t D, int causal) {

@@ -25,7 +25,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "ORDER", "WIDENED", "get", "make_inputs", "make_dout", "torch_dtype"]
+__all__ = ["Workload", "WORKLOADS", "ORDER", "WIDENED", "BACKWARD", "get", "make_inputs", "make_dout", "torch_dtype"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -66,6 +66,13 @@ class Workload:
         """
         f = 4.0 * self.B * self.H * self.M * self.N * self.D
         return f / 2 if self.causal else f
+
+    @property
+    def bwd_flops(self) -> float:
+        """Counted work of the backward pass: its five products (S recomputed,
+        dP, dV, dK, dQ) of 2*M*N*D flop each per head, i.e. 2.5 times the
+        forward's count, halved when causal."""
+        return 2.5 * self.flops
 
     @property
     def elt_bytes(self) -> int:
@@ -114,6 +121,10 @@ WORKLOADS.update({
                                 Hk=8, n_splits=0),
 })
 WIDENED = ["causal_f16_4k", "gqa_bf16_4k", "decode_gqa_bf16"]
+
+# Workloads whose backward pass the bench also times (16-bit only: the
+# backward has no fp32 kernels).
+BACKWARD = ["causal_bf16_4k", "causal_bf16_16k", "ragged_bf16_cross", "gqa_bf16_4k", "causal_f16_4k"]
 
 
 def get(name: str) -> Workload:
