@@ -52,6 +52,13 @@ def _bind(lib):
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
     ]
+    lib.fa2_oracle_fwd_local.restype = ctypes.c_int
+    lib.fa2_oracle_fwd_local.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_int,
+    ]
     lib.fa2_oracle_bwd_gqa.restype = ctypes.c_int
     lib.fa2_oracle_bwd_gqa.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -96,13 +103,16 @@ def _as_f32(x) -> np.ndarray:
 
 
 def attention(q, k, v, scale: float, causal: bool, rows: Optional[np.ndarray] = None,
-              threads: int = 0, _lib_override=None):
+              threads: int = 0, _lib_override=None, window=(-1, -1)):
     """Reference attention forward.
 
     q: [B,H,M,D], k/v: [B,Hk,N,D] with H % Hk == 0 (torch tensors or float32
     numpy arrays); query head h reads K/V head h // (H // Hk).
     rows: optional int64 array of query rows (same for every head); when
     given, outputs cover only those rows.
+    window: (left, right) sliding window; query row i sees keys
+    i - left <= j <= i + right (a negative side is unbounded), on top of
+    the causal mask.  Rows that see no key get O = 0 and L = -inf.
     Returns (o, lse) as float64 numpy arrays: o [B,H,R,D], lse [B,H,R].
     """
     qa, ka, va = _as_f32(q), _as_f32(k), _as_f32(v)
@@ -123,7 +133,12 @@ def attention(q, k, v, scale: float, causal: bool, rows: Optional[np.ndarray] = 
     o = np.empty((B, H, R, D), dtype=np.float64)
     lse = np.empty((B, H, R), dtype=np.float64)
     lib = _load() if _lib_override is None else _lib_override
-    if Hk == H:
+    wl, wr = (int(window[0]), int(window[1]))
+    if wl >= 0 or wr >= 0:
+        rc = lib.fa2_oracle_fwd_local(qa.ctypes.data, ka.ctypes.data, va.ctypes.data,
+                                      o.ctypes.data, lse.ctypes.data, B, H, Hk, M, N, D,
+                                      float(scale), int(bool(causal)), wl, wr, rows_p, R, int(threads))
+    elif Hk == H:
         rc = lib.fa2_oracle_fwd(qa.ctypes.data, ka.ctypes.data, va.ctypes.data,
                                 o.ctypes.data, lse.ctypes.data, B, H, M, N, D,
                                 float(scale), int(bool(causal)), rows_p, R, int(threads))
@@ -134,6 +149,38 @@ def attention(q, k, v, scale: float, causal: bool, rows: Optional[np.ndarray] = 
     if rc != 0:
         raise ValueError(f"fa2_oracle_fwd failed with status {rc}")
     del rows_a
+    return o, lse
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool,
+                     window=(-1, -1), threads: int = 0):
+    """Reference forward over packed variable-length sequences.
+
+    q: [H, total_q, D], k/v: [Hk, total_k, D]; sequence b owns query rows
+    cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 and keys cu_seqlens_k[b] ..
+    cu_seqlens_k[b+1] - 1 of every head, and attends only within itself.
+    Each sequence is evaluated by ``attention`` on its own rows (no
+    arithmetic here).  Returns (o [H,total_q,D], lse [H,total_q]) in
+    float64.
+    """
+    qa, ka, va = _as_f32(q), _as_f32(k), _as_f32(v)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q).tolist()]
+    ck = [int(x) for x in np.asarray(cu_seqlens_k).tolist()]
+    if qa.ndim != 3 or ka.ndim != 3 or va.ndim != 3 or len(cq) != len(ck) or len(cq) < 1:
+        raise ValueError("q, k, v must be [heads, total, D] with matching cu_seqlens")
+    H, total_q, D = qa.shape
+    o = np.zeros((H, total_q, D), dtype=np.float64)
+    lse = np.full((H, total_q), -np.inf, dtype=np.float64)
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 <= q0:
+            continue
+        if k1 <= k0:  # no keys: every row sees nothing
+            continue
+        ob, lb = attention(qa[None, :, q0:q1], ka[None, :, k0:k1], va[None, :, k0:k1], scale, causal,
+                           threads=threads, window=window)
+        o[:, q0:q1] = ob[0]
+        lse[:, q0:q1] = lb[0]
     return o, lse
 
 

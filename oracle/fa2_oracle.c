@@ -11,7 +11,9 @@
  * evaluated one query row at a time in IEEE double precision:
  *
  *   for every (b, h) and query row i, with K/V head hk = h / (H / Hk):
- *     J     = {0..N-1}, or {0..min(i, N-1)} when causal          (1)
+ *     J     = {0..N-1}, or {0..min(i, N-1)} when causal,         (1)
+ *             further cut to i - wl <= j <= i + wr by a sliding
+ *             window (wl, wr; a negative side is unbounded)
  *     s_j   = scale * sum_d q[i,d] * k[j,d]          for j in J    (2)
  *     m     = max_{j in J} s_j                                     (3)
  *     e_j   = exp(s_j - m),  l = sum_{j in J} e_j                  (4)
@@ -27,7 +29,14 @@
  *           "Writing FlashAttention 2 in Triton", Step 4 (mask keeps
  *           offs_m >= offs_n) and its bug catalogue item on the comparison
  *           direction; "FlashAttention-2 from PyTorch to Triton", the test
- *           harness's tril-masked reference.
+ *           harness's tril-masked reference.  The sliding window is the
+ *           window_size = (left, right) option of the entry point described
+ *           in "From FlashAttention to FlashAttention 2", section "Layer 1",
+ *           (-1 meaning unbounded), a change of the causal mask formula as
+ *           "Writing FlashAttention 2 in Triton" puts it (its list of next
+ *           steps); measured from the same top-left diagonal j = i.  A row
+ *           whose window holds no key gets O = 0 and L = -inf (l = 0: the
+ *           guard of that page's bug catalogue item 8 returns O = 0).
  *  (6)      L is the natural-log logsumexp of the *scaled* scores, i.e.
  *           m + log(l): "FlashAttention-2 from PyTorch to Triton", opening
  *           description of the second output L; "From FlashAttention to
@@ -68,14 +77,29 @@ int fa2_oracle_max_threads(void) {
 #endif
 }
 
-/* One query row of one (b,h) slice: steps (1)-(6) above.  `s` is scratch of
- * length >= N. */
+/* (1) the keys query row i sees: j0 <= j < j0 + n (n <= 0: none) */
+static void visible_keys(int64_t i, int64_t N, int causal, int64_t wl, int64_t wr,
+                         int64_t* j0, int64_t* n) {
+    int64_t lo = 0, hi = N - 1;
+    if (causal && i < hi) hi = i;
+    if (wr >= 0 && i + wr < hi) hi = i + wr;
+    if (wl >= 0 && i - wl > lo) lo = i - wl;
+    *j0 = lo;
+    *n = hi - lo + 1;
+}
+
+/* One query row of one (b,h) slice: steps (2)-(6) above over the visible
+ * keys j0 .. j0 + n_vis - 1.  `s` is scratch of length >= N. */
 static void oracle_row(const float* qi, const float* kbh, const float* vbh,
-                       double* orow, double* lse_out, int64_t i, int64_t N,
-                       int64_t D, double scale, int causal, double* s) {
-    /* (1) visible keys */
-    int64_t n_vis = N;
-    if (causal) n_vis = (i + 1 < N) ? (i + 1) : N;
+                       double* orow, double* lse_out, int64_t j0, int64_t n_vis,
+                       int64_t D, double scale, double* s) {
+    if (n_vis <= 0) {  /* no visible key: l = 0 */
+        for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
+    kbh += j0 * D;
+    vbh += j0 * D;
 
     /* (2) scores and (3) row maximum */
     double m = -INFINITY;
@@ -109,17 +133,17 @@ static void oracle_row(const float* qi, const float* kbh, const float* vbh,
 
 /*
  * q: [B,H,M,D], k and v: [B,Hk,N,D], all contiguous row-major floats;
- * H % Hk == 0 (Hk >= 1).
+ * H % Hk == 0 (Hk >= 1).  wl, wr: sliding window (negative: unbounded).
  * rows == NULL: every query row; o is [B,H,M,D] and lse is [B,H,M].
  * rows != NULL: only the n_rows listed rows (each in [0, M)), the same rows
  *   for every (b,h); o is [B,H,n_rows,D] and lse is [B,H,n_rows].
  * n_threads <= 0 uses the OpenMP default.
  * Returns 0 on success, nonzero on invalid arguments or allocation failure.
  */
-int fa2_oracle_fwd_gqa(const float* q, const float* k, const float* v, double* o,
-                       double* lse, int64_t B, int64_t H, int64_t Hk, int64_t M,
-                       int64_t N, int64_t D, double scale, int causal,
-                       const int64_t* rows, int64_t n_rows, int n_threads) {
+int fa2_oracle_fwd_local(const float* q, const float* k, const float* v, double* o,
+                         double* lse, int64_t B, int64_t H, int64_t Hk, int64_t M,
+                         int64_t N, int64_t D, double scale, int causal, int64_t wl,
+                         int64_t wr, const int64_t* rows, int64_t n_rows, int n_threads) {
     if (!q || !k || !v || !o || !lse) return FA2_ORACLE_EINVAL;
     if (B < 0 || H < 0 || M < 0 || N <= 0 || D <= 0) return FA2_ORACLE_EINVAL;
     if (Hk < 1 || H % Hk != 0) return FA2_ORACLE_EINVAL;
@@ -156,13 +180,23 @@ int fa2_oracle_fwd_gqa(const float* q, const float* k, const float* v, double* o
             const int64_t i = rows ? rows[r] : r;
             const int64_t b = bh / H, h = bh % H;
             const int64_t kvh = b * Hk + h / group; /* (hk) */
+            int64_t j0, n_vis;
+            visible_keys(i, N, causal, wl, wr, &j0, &n_vis);
             oracle_row(q + (bh * M + i) * D, k + kvh * N * D, v + kvh * N * D,
-                       o + (bh * R + r) * D, lse + bh * R + r, i, N, D, scale,
-                       causal, s);
+                       o + (bh * R + r) * D, lse + bh * R + r, j0, n_vis, D, scale, s);
         }
         free(s);
     }
     return status;
+}
+
+/* No sliding window. */
+int fa2_oracle_fwd_gqa(const float* q, const float* k, const float* v, double* o,
+                       double* lse, int64_t B, int64_t H, int64_t Hk, int64_t M,
+                       int64_t N, int64_t D, double scale, int causal,
+                       const int64_t* rows, int64_t n_rows, int n_threads) {
+    return fa2_oracle_fwd_local(q, k, v, o, lse, B, H, Hk, M, N, D, scale, causal, -1, -1,
+                                rows, n_rows, n_threads);
 }
 
 /* Multi-head attention: every query head has its own K/V head (Hk == H). */

@@ -305,7 +305,137 @@ def check_brute(attn, M, N, D, causal):
     close(lse, lb, 1e-13)
 
 
+# ------------------------------------------------------------ sliding window
+
+def window_bounds(i, N, causal, wl, wr):
+    """First and last key row i sees (lo > hi: none), written out from the
+    statement of the window: i - wl <= j <= i + wr, j <= i when causal."""
+    lo = 0 if wl < 0 else max(0, i - wl)
+    hi = N - 1
+    if causal:
+        hi = min(hi, i)
+    if wr >= 0:
+        hi = min(hi, i + wr)
+    return lo, hi
+
+
+WINDOWS = [((2, 1), False), ((0, 0), False), ((3, -1), False), ((-1, 2), False), ((1, 5), True),
+           ((4, -1), True), ((2, -1), False)]
+
+
+def check_window_constant_scores(attn):
+    # Q = 0: uniform weights over each row's window, so O is the mean of the
+    # window's V rows and L the log of its size; M > N leaves the last rows
+    # of the (2, -1) window empty (O = 0, L = -inf).
+    M, N = 20, 8
+    q = np.zeros((1, 2, M, 64), np.float32)
+    k, v = rnd((1, 2, N, 64), 80), rnd((1, 2, N, 64), 81)
+    v64 = v.astype(np.float64)
+    for (wl, wr), causal in WINDOWS:
+        o, lse = attn(q, k, v, 0.125, causal, window=(wl, wr))
+        for i in range(M):
+            lo, hi = window_bounds(i, N, causal, wl, wr)
+            if hi < lo:
+                close(o[:, :, i], 0.0, 0)
+                assert np.all(lse[:, :, i] == -np.inf)
+            else:
+                close(o[:, :, i], v64[:, :, lo:hi + 1].mean(axis=2), 1e-14)
+                close(lse[:, :, i], math.log(hi - lo + 1), 1e-14)
+
+
+def check_window_torch(attn):
+    # torch fp64 SDPA with the band mask spelled out (rows non-empty)
+    M, N = 45, 60
+    q, k, v = rnd((1, 2, M, 64), 82), rnd((1, 2, N, 64), 83), rnd((1, 2, N, 64), 84)
+    for (wl, wr), causal in [((7, 3), False), ((16, -1), True), ((-1, 5), False), ((0, 0), False)]:
+        o, lse = attn(q, k, v, 0.125, causal, window=(wl, wr))
+        mask = torch.zeros(M, N, dtype=torch.bool)
+        for i in range(M):
+            lo, hi = window_bounds(i, N, causal, wl, wr)
+            mask[i, lo:hi + 1] = True
+        q64, k64, v64 = (torch.from_numpy(x.astype(np.float64)) for x in (q, k, v))
+        o_ref = torch.nn.functional.scaled_dot_product_attention(q64, k64, v64, attn_mask=mask, scale=0.125)
+        s = (q64 @ k64.transpose(-1, -2) * 0.125).masked_fill(~mask, float("-inf"))
+        close(o, o_ref.numpy(), 1e-12)
+        close(lse, torch.logsumexp(s, dim=-1).numpy(), 1e-12)
+
+
+def check_window_limits(attn):
+    # an unbounded window is no window; a right bound of 0 is the causal mask;
+    # bounds past the sequence change nothing
+    q, k, v = rnd((1, 2, 30, 64), 85), rnd((1, 2, 41, 64), 86), rnd((1, 2, 41, 64), 87)
+    o0, l0 = attn(q, k, v, 0.2, False)
+    oc, lc = attn(q, k, v, 0.2, True)
+    for window, causal, (oe, le) in [((-1, -1), False, (o0, l0)), ((100, 100), False, (o0, l0)),
+                                     ((-1, 0), False, (oc, lc)), ((100, 0), False, (oc, lc)),
+                                     ((100, 7), True, (oc, lc))]:
+        o, lse = attn(q, k, v, 0.2, causal, window=window)
+        np.testing.assert_array_equal(o, oe)
+        np.testing.assert_array_equal(lse, le)
+
+
+def brute_force_window(q, k, v, scale, causal, wl, wr, digits=50):
+    """The 50-digit brute force over each row's window."""
+    B, H, M, D = q.shape
+    N = k.shape[2]
+    O = np.zeros((B, H, M, D))
+    L = np.zeros((B, H, M))
+    for i in range(M):
+        lo, hi = window_bounds(i, N, causal, wl, wr)
+        ob, lb = brute_force(q[:, :, i:i + 1], k[:, :, lo:hi + 1], v[:, :, lo:hi + 1], scale, False, digits)
+        O[:, :, i] = ob[:, :, 0]
+        L[:, :, i] = lb[:, :, 0]
+    return O, L
+
+
+def check_window_brute(attn):
+    q, k, v = rnd((1, 1, 7, 6), 88, 2.0), rnd((1, 1, 9, 6), 89, 2.0), rnd((1, 1, 9, 6), 90)
+    for (wl, wr), causal in [((2, 1), False), ((1, -1), True)]:
+        o, lse = attn(q, k, v, 0.35, causal, window=(wl, wr))
+        ob, lb = brute_force_window(q, k, v, 0.35, causal, wl, wr)
+        close(o, ob, 1e-13)
+        close(lse, lb, 1e-13)
+
+
 # ---------------------------------------------------------------- the pytests
+
+def test_window_constant_scores():
+    check_window_constant_scores(oracle.attention)
+
+
+def test_window_matches_torch_band_mask():
+    check_window_torch(oracle.attention)
+
+
+def test_window_limits():
+    check_window_limits(oracle.attention)
+
+
+def test_window_matches_decimal_brute_force():
+    check_window_brute(oracle.attention)
+
+
+def test_varlen_equals_dense_per_sequence():
+    # packed head-major sequences of different lengths: each sequence equals
+    # the dense oracle on its own rows; a sequence with no keys gives O = 0,
+    # L = -inf; an empty sequence is skipped
+    lens_q, lens_k = [5, 0, 17, 9], [7, 3, 17, 0]
+    cq, ck = np.cumsum([0] + lens_q), np.cumsum([0] + lens_k)
+    q, k, v = rnd((3, cq[-1], 64), 91), rnd((1, ck[-1], 64), 92), rnd((1, ck[-1], 64), 93)
+    for causal, window in [(False, (-1, -1)), (True, (-1, -1)), (False, (3, 2))]:
+        o, lse = oracle.attention_varlen(q, k, v, cq, ck, 0.125, causal, window)
+        for b in range(4):
+            q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+            if q1 == q0:
+                continue
+            if k1 == k0:
+                assert np.all(o[:, q0:q1] == 0) and np.all(lse[:, q0:q1] == -np.inf)
+                continue
+            ob, lb = oracle.attention(q[None, :, q0:q1], np.repeat(k[None, :, k0:k1], 3, 1),
+                                      np.repeat(v[None, :, k0:k1], 3, 1), 0.125, causal, window=window)
+            np.testing.assert_array_equal(o[:, q0:q1], ob[0])
+            np.testing.assert_array_equal(lse[:, q0:q1], lb[0])
+
 
 def test_single_key_gives_value_row_and_score():
     check_single_key(oracle.attention)
@@ -426,7 +556,8 @@ ALL_PINS = (
     [check_single_key, check_causal_prefix_means, check_causal_row_zero, check_weights_sum_to_one,
      check_identity_values, check_large_magnitude_two_keys, check_key_shift,
      check_joint_key_permutation, check_linear_in_values, check_slices_independent,
-     check_gqa_equals_expanded_heads, check_mqa_constant_scores, check_gqa_torch]
+     check_gqa_equals_expanded_heads, check_mqa_constant_scores, check_gqa_torch,
+     check_window_constant_scores, check_window_torch, check_window_limits, check_window_brute]
     + [lambda a, N=N: check_constant_scores(a, N) for N in (1, 37, 65)]
     + [lambda a, c=c: check_geometric_scores(a, c) for c in (0.05, 0.7)]
     + [lambda a, s=s, c=c: check_torch(a, *s, c) for s in LIB_SHAPES[:4] for c in (False, True)]
@@ -438,8 +569,12 @@ MUTANTS = {
     "scale dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
     "log base 2": ("*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
     "max missing from L": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
-    "diagonal excluded": ("n_vis = (i + 1 < N) ? (i + 1) : N;", "n_vis = (i < N) ? (i > 0 ? i : 1) : N;"),
-    "causal reversed": ("if (causal) n_vis =", "if (!causal) n_vis ="),
+    "diagonal excluded": ("if (causal && i < hi) hi = i;", "if (causal && i - 1 < hi) hi = i - 1;"),
+    "causal reversed": ("if (causal && i < hi) hi = i;", "if (causal && i > lo) lo = i;"),
+    "window left bound off by one": ("if (wl >= 0 && i - wl > lo) lo = i - wl;",
+                                     "if (wl >= 0 && i - wl + 1 > lo) lo = i - wl + 1;"),
+    "window right bound ignored": ("if (wr >= 0 && i + wr < hi) hi = i + wr;", ""),
+    "empty window gives L = 0": ("*lse_out = -INFINITY;\n        return;", "*lse_out = 0.0;\n        return;"),
     "no normalisation": ("orow[d] /= l;", "orow[d] /= 1.0;"),
     "weights misaligned with values": ("const double e = s[j];", "const double e = s[n_vis - 1 - j];"),
     "key row misindexed": ("const float* kj = kbh + j * D;", "const float* kj = kbh + (n_vis - 1 - j) * D;"),
@@ -465,8 +600,8 @@ def _build_mutant(tmp_path, name, edit):
 def test_pins_catch_planted_mistakes(tmp_path, name):
     lib = _build_mutant(tmp_path, name, MUTANTS[name])
 
-    def mutant(q, k, v, scale, causal, rows=None):
-        return oracle.attention(q, k, v, scale, causal, rows=rows, _lib_override=lib)
+    def mutant(q, k, v, scale, causal, rows=None, window=(-1, -1)):
+        return oracle.attention(q, k, v, scale, causal, rows=rows, _lib_override=lib, window=window)
 
     failures = 0
     for pin in ALL_PINS:
