@@ -6,11 +6,12 @@ There is no CPU fallback: if the library is missing, importing the binding
 raises.
 
 ``fa2_fwd``, ``fa2_fwd_ex``, ``fa2_fwd_workspace_bytes``,
-``fa2_fwd_num_splits`` and ``fa2_bwd`` mirror the C entry points of
-``include/fa2.h`` one to one (raw device pointers and sizes).  ``forward`` and
-``backward`` are the tensor-level conveniences that allocate outputs (and any
-split-K/V workspace) with torch and call the library on the current stream;
-``attention`` wraps both in a ``torch.autograd.Function``.
+``fa2_fwd_num_splits``, ``fa2_fwd_local``, ``fa2_fwd_varlen`` and ``fa2_bwd``
+mirror the C entry points of ``include/fa2.h`` one to one (raw device
+pointers and sizes).  ``forward``, ``forward_varlen`` and ``backward`` are the
+tensor-level conveniences that allocate outputs (and any split-K/V
+workspace) with torch and call the library on the current stream;
+``attention`` wraps forward and backward in a ``torch.autograd.Function``.
 """
 from __future__ import annotations
 
@@ -20,8 +21,9 @@ import os
 
 __all__ = ["FA2_DTYPE_F32", "FA2_DTYPE_BF16", "FA2_DTYPE_F16", "FA2_OK", "FA2_ERR_INVALID_ARGUMENT",
            "FA2_ERR_UNSUPPORTED", "FA2_ERR_LAUNCH", "FA2_ERR_NO_DEVICE", "FA2_MAX_SPLITS", "Fa2Error",
-           "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_workspace_bytes", "fa2_fwd_num_splits", "fa2_bwd",
-           "fa2_status_string", "forward", "backward", "attention", "library_path", "EXPORTED_SYMBOLS"]
+           "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_workspace_bytes", "fa2_fwd_num_splits", "fa2_fwd_local",
+           "fa2_fwd_varlen", "fa2_bwd", "fa2_status_string", "forward", "forward_varlen", "backward",
+           "attention", "library_path", "EXPORTED_SYMBOLS"]
 
 FA2_DTYPE_F32 = 0
 FA2_DTYPE_BF16 = 1
@@ -35,8 +37,8 @@ FA2_ERR_NO_DEVICE = 4
 
 FA2_MAX_SPLITS = 128
 
-EXPORTED_SYMBOLS = ("fa2_bwd", "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_num_splits", "fa2_fwd_workspace_bytes",
-                    "fa2_status_string")
+EXPORTED_SYMBOLS = ("fa2_bwd", "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_local", "fa2_fwd_num_splits",
+                    "fa2_fwd_varlen", "fa2_fwd_workspace_bytes", "fa2_status_string")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa2.so")
@@ -92,6 +94,12 @@ def _load():
     lib.fa2_fwd_workspace_bytes.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
     lib.fa2_fwd_num_splits.restype = ctypes.c_int
     lib.fa2_fwd_num_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int]
+    lib.fa2_fwd_local.restype = ctypes.c_int
+    lib.fa2_fwd_local.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.fa2_fwd_varlen.restype = ctypes.c_int
+    lib.fa2_fwd_varlen.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 7 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     lib.fa2_bwd.restype = ctypes.c_int
     lib.fa2_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
@@ -133,6 +141,24 @@ def fa2_fwd_num_splits(B: int, H: int, Hk: int, M: int, N: int, D: int, causal: 
     return int(_lib.fa2_fwd_num_splits(B, H, Hk, M, N, D, causal, dtype))
 
 
+def fa2_fwd_local(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Hk: int, M: int, N: int, D: int,
+                  scale: float, causal: int, window_left: int, window_right: int, dtype: int,
+                  stream: int | None) -> int:
+    """Direct call of the sliding-window C entry point; pointers are integers.
+    Returns the fa2_status code."""
+    return int(_lib.fa2_fwd_local(q, k, v, o, lse, B, H, Hk, M, N, D, scale, causal, window_left,
+                                  window_right, dtype, stream))
+
+
+def fa2_fwd_varlen(q: int, k: int, v: int, o: int, lse: int, cu_seqlens_q: int, cu_seqlens_k: int, B: int,
+                   H: int, Hk: int, total_q: int, total_k: int, max_seqlen_q: int, D: int, scale: float,
+                   causal: int, window_left: int, window_right: int, dtype: int, stream: int | None) -> int:
+    """Direct call of the packed-sequence C entry point; pointers are
+    integers.  Returns the fa2_status code."""
+    return int(_lib.fa2_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, Hk, total_q, total_k,
+                                   max_seqlen_q, D, scale, causal, window_left, window_right, dtype, stream))
+
+
 def fa2_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, delta: int,
             B: int, H: int, Hk: int, M: int, N: int, D: int, scale: float, causal: int, dtype: int,
             stream: int | None) -> int:
@@ -158,7 +184,7 @@ def _dtype_code(t):
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
-            n_splits: int = 1, workspace=None):
+            n_splits: int = 1, workspace=None, window=(-1, -1)):
     """Attention forward on the current CUDA/HIP stream.
 
     q: [B,H,M,D], k/v: [B,Hk,N,D] contiguous device tensors of one dtype
@@ -168,6 +194,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     over all keys, 0 = library's choice, >1 = split K/V with a combine kernel;
     the workspace it needs is allocated with torch unless ``workspace`` (a
     device tensor of at least ``fa2_fwd_workspace_bytes`` bytes) is given.
+    ``window`` = (left, right): sliding window (fa2_fwd_local; -1 leaves a
+    side unbounded); it cannot be combined with split K/V.
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -192,6 +220,17 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     elif lse.shape != (B, H, M) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor of shape [B,H,M]")
     code = _dtype_code(q)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    wl, wr = int(window[0]), int(window[1])
+    if (wl, wr) != (-1, -1):
+        if n_splits != 1:
+            raise ValueError("a sliding window runs unsplit (n_splits=1)")
+        with torch.cuda.device(q.device):
+            st = fa2_fwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, Hk, M, N, D, float(scale), int(bool(causal)), wl, wr, code, stream)
+        if st != FA2_OK:
+            raise Fa2Error(st)
+        return out, lse
     splits = fa2_fwd_num_splits(B, H, Hk, M, N, D, int(bool(causal)), code) if n_splits == 0 else int(n_splits)
     ws_ptr, ws_size = None, 0
     if splits > 1:
@@ -201,11 +240,56 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         ws_ptr, ws_size = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
         st = fa2_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                         B, H, Hk, M, N, D, float(scale), int(bool(causal)), code, splits,
                         ws_ptr, ws_size, stream)
+    if st != FA2_OK:
+        raise Fa2Error(st)
+    return out, lse
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
+                   scale: float | None = None, window=(-1, -1), out=None, lse=None):
+    """Forward over packed variable-length sequences (fa2_fwd_varlen).
+
+    q: [H, total_q, D], k/v: [Hk, total_k, D] contiguous device tensors of one
+    dtype; cu_seqlens_q / cu_seqlens_k: int32 device tensors of B + 1
+    offsets (sequence b owns rows cu[b] .. cu[b+1]-1 of every head);
+    max_seqlen_q bounds every sequence's query count.  Returns
+    (o [H, total_q, D], lse [H, total_q] float32).
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 3-D tensor [heads, total, D]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32 or t.dim() != 1
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous 1-D int32 device tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must hold the same number (B + 1) of offsets")
+    H, total_q, D = q.shape
+    Hk, total_k = k.shape[0], k.shape[1]
+    if k.shape != (Hk, total_k, D) or v.shape != k.shape or Hk < 1 or H % Hk:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    B = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa2_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Hk, total_q, total_k,
+                            int(max_seqlen_q), D, float(scale), int(bool(causal)), int(window[0]),
+                            int(window[1]), _dtype_code(q), stream)
     if st != FA2_OK:
         raise Fa2Error(st)
     return out, lse

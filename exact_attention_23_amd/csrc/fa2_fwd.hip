@@ -74,29 +74,86 @@ struct FwdParams {
     float* lse;
     float* ws_o;          // split K/V: partial O [n_splits, BH, M, D] fp32, else null
     float* ws_l;          // split K/V: partial L [n_splits, BH, M] fp32, else null
+    const int* cu_q;      // packed sequences: query row offsets [B + 1] (device), else null
+    const int* cu_k;      // packed sequences: key row offsets [B + 1]
+    int total_q, total_k; // packed sequences: rows per head of q (o, lse) and of k (v)
     int BH;               // batch * query heads
     int H;                // query heads
+    int Hk;               // K/V heads
     int G;                // query heads per K/V head (H / Hk)
-    int M, N;
+    int M, N;             // dense: query rows and keys per head
     int n_qt;             // query tiles per head
     int tiles_per_split;  // K/V tiles per split (at least all of them when unsplit)
+    int wl, wr;           // sliding window: keys i - wl .. i + wr (-1: unbounded side)
     float c_log2;         // scale * log2(e)
 };
 
-// One workgroup's task: query tile qt of head bh, reading K/V head bkv
-// (query head h uses K/V head h / G, "From FlashAttention to FlashAttention 2",
-// section "Layer 8"), over K/V tiles [t_begin, t_begin + n_kv) of its split.
+// Which keys a query row sees.
+constexpr int kMaskNone = 0;    // all of them
+constexpr int kMaskCausal = 1;  // key j visible to query i iff j <= i (top-left)
+constexpr int kMaskLocal = 2;   // sliding window i - wl <= j <= i + wr, either side unbounded when -1
+                                // (causal with a window is wr = 0)
+
+// First and last key query row i of a sequence of N keys sees (lo > hi: none).
+template <int MASK>
+__device__ __forceinline__ int key_lo(const FwdParams& p, int i) {
+    return (MASK == kMaskLocal && p.wl >= 0) ? max(0, i - p.wl) : 0;
+}
+template <int MASK>
+__device__ __forceinline__ int key_hi(const FwdParams& p, int i, int N) {
+    int hi = N - 1;
+    if (MASK == kMaskCausal) hi = min(hi, i);
+    if (MASK == kMaskLocal && p.wr >= 0) hi = min(hi, i + p.wr);
+    return hi;
+}
+
+// The (batch, head) sequence a workgroup works on: a head of the dense
+// [B, H, M, D] layout (cu_q == null), or sequence b of the packed layout
+// [H, total_q, D] / [Hk, total_k, D] whose rows cu_q[b] .. cu_q[b + 1] - 1
+// (keys cu_k[b] .. cu_k[b + 1] - 1) belong to it.  Offsets outside
+// [0, total] are clamped, so a malformed offset array cannot address memory
+// past the tensors.
+struct SeqView {
+    int64_t q_row0;   // row of q, o and lse that holds the sequence's query 0
+    int64_t kv_row0;  // row of k and v that holds its key 0
+    int M, N;         // query rows and keys of the sequence
+};
+__device__ __forceinline__ SeqView seq_view(const FwdParams& p, int bh, int bkv) {
+    SeqView v;
+    if (p.cu_q == nullptr) {
+        v.M = p.M;
+        v.N = p.N;
+        v.q_row0 = (int64_t)bh * p.M;
+        v.kv_row0 = (int64_t)bkv * p.N;
+    } else {
+        const int b = bh / p.H, h = bh - b * p.H, hk = bkv - b * p.Hk;
+        const int q0 = min(max(p.cu_q[b], 0), p.total_q), q1 = min(max(p.cu_q[b + 1], q0), p.total_q);
+        const int k0 = min(max(p.cu_k[b], 0), p.total_k), k1 = min(max(p.cu_k[b + 1], k0), p.total_k);
+        v.M = q1 - q0;
+        v.N = k1 - k0;
+        v.q_row0 = (int64_t)h * p.total_q + q0;
+        v.kv_row0 = (int64_t)hk * p.total_k + k0;
+    }
+    return v;
+}
+
+// One workgroup's task: query tile qt of sequence sv (head bh), reading K/V
+// head bkv (query head h uses K/V head h / G, "From FlashAttention to
+// FlashAttention 2", section "Layer 8"), over K/V tiles
+// [t_begin, t_begin + n_kv) of its split.
 struct WgTask {
     int bh, bkv, qt, split;
-    int t_begin;    // first K/V tile of the split
-    int n_kv;       // K/V tiles of this workgroup (0 for a split past the diagonal)
-    int n_kv_full;  // K/V tiles the query tile needs when unsplit
+    SeqView sv;
+    int t_begin;  // first K/V tile of the workgroup (of its split)
+    int n_kv;     // K/V tiles of this workgroup (0 for a split past the diagonal)
 };
 
 // Grid order: split-major, then query tile (heaviest first when causal), then
 // batch*head fastest, so that the tiles of one head spread over the XCDs in
-// step and every XCD gets the same mix of heavy and light tiles.
-template <bool CAUSAL, bool SPLIT>
+// step and every XCD gets the same mix of heavy and light tiles.  The tiles a
+// workgroup needs run from the first key its first row sees to the last key
+// its last row sees.
+template <int MASK, bool SPLIT>
 __device__ __forceinline__ WgTask wg_task(const FwdParams& p, int BM, int BN) {
     WgTask t;
     const int wg = blockIdx.x;
@@ -109,24 +166,51 @@ __device__ __forceinline__ WgTask wg_task(const FwdParams& p, int BM, int BN) {
     }
     t.bh = r % p.BH;
     t.qt = r / p.BH;
-    if (CAUSAL) t.qt = p.n_qt - 1 - t.qt;
+    if (MASK == kMaskCausal) t.qt = p.n_qt - 1 - t.qt;
     // bh = (b * Hk + hk) * G + g for query head h = hk * G + g
     t.bkv = p.G == 1 ? t.bh : t.bh / p.G;
-    const int kv_end = CAUSAL ? min(p.N, t.qt * BM + BM) : p.N;
-    t.n_kv_full = (kv_end + BN - 1) / BN;
-    t.t_begin = t.split * p.tiles_per_split;
-    t.n_kv = max(0, min(t.n_kv_full - t.t_begin, p.tiles_per_split));
+    t.sv = seq_view(p, t.bh, t.bkv);
+    const int r0 = t.qt * BM, r1 = min(r0 + BM, t.sv.M) - 1;
+    int lo_t = 0, hi_t = 0;  // the query tile's K/V tiles [lo_t, hi_t)
+    if (r0 <= r1) {
+        const int klo = key_lo<MASK>(p, r0), khi = key_hi<MASK>(p, r1, t.sv.N);
+        if (klo <= khi) {
+            lo_t = klo / BN;
+            hi_t = khi / BN + 1;
+        }
+    }
+    t.t_begin = lo_t + t.split * p.tiles_per_split;
+    t.n_kv = max(0, min(hi_t - t.t_begin, p.tiles_per_split));
     return t;
 }
 
-// K/V tiles (of the workgroup's range) that a wave whose rows start at qw0
-// needs: causal rows stop at their diagonal, rows past M need none.
-template <bool CAUSAL>
-__device__ __forceinline__ int wave_tiles(const FwdParams& p, const WgTask& t, int qw0, int rows, int BN) {
-    if (qw0 >= p.M) return 0;
-    int n = t.n_kv_full;
-    if (CAUSAL) n = min(n, (min(p.N, qw0 + rows) + BN - 1) / BN);
-    return max(0, min(n - t.t_begin, t.n_kv));
+// The workgroup's K/V tiles [first, end) (indices from t_begin) that a wave
+// whose rows start at qw0 needs: each row only needs the tiles of its keys;
+// rows past M need none.
+struct WaveRange {
+    int first, end;
+};
+template <int MASK>
+__device__ __forceinline__ WaveRange wave_tiles(const FwdParams& p, const WgTask& t, int qw0, int rows, int BN) {
+    WaveRange w{0, 0};
+    const int r1 = min(qw0 + rows, t.sv.M) - 1;
+    if (qw0 > r1) return w;
+    const int klo = key_lo<MASK>(p, qw0), khi = key_hi<MASK>(p, r1, t.sv.N);
+    if (klo > khi) return w;
+    w.first = max(klo / BN - t.t_begin, 0);
+    w.end = max(min(khi / BN + 1 - t.t_begin, t.n_kv), w.first);
+    return w;
+}
+
+// Does K/V tile kbase .. kbase + BN - 1 need a mask for the rows qa .. qb of a
+// wave: it runs past N, or past the last key of the first row, or starts
+// before the first key of the last row.
+template <int MASK>
+__device__ __forceinline__ bool tile_needs_mask(const FwdParams& p, int kbase, int BN, int N, int qa, int qb) {
+    if (kbase + BN > N) return true;
+    if (MASK != kMaskNone && kbase + BN - 1 > key_hi<MASK>(p, qa, N)) return true;
+    if (MASK == kMaskLocal && kbase < key_lo<MASK>(p, qb)) return true;
+    return false;
 }
 
 // Split-K/V partial result of one query row (the lane's 4 consecutive O values
@@ -191,7 +275,7 @@ __device__ __forceinline__ int swz_v(int r) {
 }
 
 
-template <typename E, int D, int BN, int NW, int QB, int WAVES_PER_SIMD, bool CAUSAL, bool SPLIT>
+template <typename E, int D, int BN, int NW, int QB, int WAVES_PER_SIMD, int MASK, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64, WAVES_PER_SIMD)
 fa2_fwd_half_kernel(const FwdParams p) {
     using T = HalfTraits<D, BN, NW, QB>;
@@ -202,7 +286,6 @@ fa2_fwd_half_kernel(const FwdParams p) {
     const E* __restrict__ V = static_cast<const E*>(p.v);
     E* __restrict__ O = static_cast<E*>(p.o);
     float* __restrict__ LSE = p.lse;
-    const int M = p.M, N = p.N;
     const float c_log2 = p.c_log2;
     // Two K/V tile buffers, each BN rows x D bf16 (rows unpadded, chunks
     // swizzled).  They are separate arrays, and the loop below is unrolled by
@@ -220,18 +303,19 @@ fa2_fwd_half_kernel(const FwdParams p) {
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
-    const WgTask task = wg_task<CAUSAL, SPLIT>(p, T::kBM, BN);
-    const int bh = task.bh;
+    const WgTask task = wg_task<MASK, SPLIT>(p, T::kBM, BN);
+    const int M = task.sv.M, N = task.sv.N;
     const int qw0 = task.qt * T::kBM + wave * T::kQPW;  // first query row of this wave
+    const int qw1 = min(qw0 + T::kQPW, M) - 1;          // last one
 
-    const E* Qh = Q + (int64_t)bh * M * D;
-    const E* Kh = K + (int64_t)task.bkv * N * D;
-    const E* Vh = V + (int64_t)task.bkv * N * D;
+    const E* Qh = Q + task.sv.q_row0 * D;
+    const E* Kh = K + task.sv.kv_row0 * D;
+    const E* Vh = V + task.sv.kv_row0 * D;
 
     // local tile kt is K/V tile kv_t0 + kt of the head
     const int kv_t0 = task.t_begin;
     const int n_kv = task.n_kv;
-    const int n_kv_wave = wave_tiles<CAUSAL>(p, task, qw0, T::kQPW, BN);
+    const WaveRange wtiles = wave_tiles<MASK>(p, task, qw0, T::kQPW, BN);
 
     // ---- Q fragments: B operand of S^T = K Q^T (lane = query, 8 d values)
     V8 qf[QB][T::kDS];
@@ -300,7 +384,7 @@ fa2_fwd_half_kernel(const FwdParams p) {
 
     // kt: K/V tile of the head (only the mask uses it)
     auto compute_tile = [&](auto mask_tag, int kt, const char* klds, const char* vlds) {
-        constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr bool BOUNDARY = decltype(mask_tag)::value;
         // S^T = K Q^T for BN keys x QPW queries; K fragments are read one
         // k-step ahead of the MFMAs that use them.
         floatx16 sacc[T::kKB][QB];
@@ -329,21 +413,24 @@ fa2_fwd_half_kernel(const FwdParams p) {
                     sacc[kb][qb] = Half<E>::mfma(kf[s & 1][kb], qf[qb][s], sacc[kb][qb]);
         }
 
-        // boundary tiles only: keys past N, and (causal) keys after the
-        // query.  Key kbase + 32 kb + acc_row(r, h) is visible iff its
-        // compile-time part 32 kb + 8 (r / 4) + r % 4 is <= lim.
-        if constexpr (MASK) {
+        // boundary tiles only: keys past N, and keys outside the query's
+        // causal or window range.  Key kbase + 32 kb + acc_row(r, h) is
+        // visible iff its compile-time part 32 kb + 8 (r / 4) + r % 4 lies in
+        // [lim_lo, lim].
+        if constexpr (BOUNDARY) {
             const int kbase = kt * BN;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                int lim = N - 1 - kbase;
-                if (CAUSAL) lim = min(lim, qw0 + 32 * qb + l32 - kbase);
-                lim -= 4 * h;
+                const int query = qw0 + 32 * qb + l32;
+                const int lim = key_hi<MASK>(p, query, N) - kbase - 4 * h;
+                const int lim_lo = key_lo<MASK>(p, query) - kbase - 4 * h;
 #pragma unroll
                 for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][qb][r] = -INFINITY;
+                    for (int r = 0; r < 16; ++r) {
+                        const int idx = 32 * kb + 8 * (r >> 2) + (r & 3);
+                        if (idx > lim || (MASK == kMaskLocal && idx < lim_lo)) sacc[kb][qb][r] = -INFINITY;
+                    }
             }
         }
 
@@ -436,12 +523,12 @@ fa2_fwd_half_kernel(const FwdParams p) {
     if (n_kv > 0) issue_tile(0, sK0, sV0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // A tile needs masking if it runs past N or (causal) reaches past the
-    // wave's first query row; all other tiles take the mask-free path.
+    // A tile needs masking if it runs past N or cuts into some row's causal
+    // or window range; all other tiles take the mask-free path.
     auto run_tile = [&](int kt, const char* klds, const char* vlds) {
-        if (kt >= n_kv_wave) return;
+        if (kt < wtiles.first || kt >= wtiles.end) return;
         const int kbase = (kv_t0 + kt) * BN;
-        if (kbase + BN > N || (CAUSAL && kbase + BN - 1 > qw0))
+        if (tile_needs_mask<MASK>(p, kbase, BN, N, qw0, qw1))
             compute_tile(std::true_type{}, kv_t0 + kt, klds, vlds);
         else
             compute_tile(std::false_type{}, kv_t0 + kt, klds, vlds);
@@ -481,7 +568,7 @@ fa2_fwd_half_kernel(const FwdParams p) {
                     }
                 if (h == 0) *partial_l(p, task, query) = lse;
             } else {
-                E* orow = O + ((int64_t)bh * M + query) * D;
+                E* orow = O + (task.sv.q_row0 + query) * D;
 #pragma unroll
                 for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
@@ -492,7 +579,7 @@ fa2_fwd_half_kernel(const FwdParams p) {
                         w[1] = pack2<E>(oacc[db][qb][4 * g + 2] * inv, oacc[db][qb][4 * g + 3] * inv);
                         *reinterpret_cast<uint2*>(orow + d) = make_uint2(w[0], w[1]);
                     }
-                if (h == 0) LSE[(int64_t)bh * M + query] = lse;
+                if (h == 0) LSE[task.sv.q_row0 + query] = lse;
             }
         }
     }
@@ -568,7 +655,9 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
-    const WgTask task = wg_task<CAUSAL, SPLIT>(p, T::kBM, BN);
+    // (dense layout and no window: the ping-pong kernel serves fa2_fwd_ex only)
+    constexpr int MASK = CAUSAL ? kMaskCausal : kMaskNone;
+    const WgTask task = wg_task<MASK, SPLIT>(p, T::kBM, BN);
     const int bh = task.bh;
     const int qw0 = task.qt * T::kBM + 32 * (2 * (wave & 3) + grp);  // first query row of this wave
 
@@ -579,7 +668,7 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
     // local tile t is K/V tile kv_t0 + t of the head
     const int kv_t0 = task.t_begin;
     const int n_kv = task.n_kv;
-    const int n_w = wave_tiles<CAUSAL>(p, task, qw0, 32, BN);  // tiles this wave needs
+    const int n_w = wave_tiles<MASK>(p, task, qw0, 32, BN).end;  // tiles this wave needs (from tile 0)
 
     // ---- Q fragments: B operand of S^T = K Q^T (lane = query, 8 d values)
     V8 qf[T::kDS];
@@ -847,7 +936,7 @@ struct F32Traits {
     static constexpr size_t kLdsBytes = 2 * (kKElems + kVElems) * sizeof(float);
 };
 
-template <int D, int BN, int NW, bool CAUSAL, bool SPLIT>
+template <int D, int BN, int NW, int MASK, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64)
 fa2_fwd_f32_kernel(const FwdParams p) {
     using T = F32Traits<D, BN, NW>;
@@ -856,7 +945,6 @@ fa2_fwd_f32_kernel(const FwdParams p) {
     const float* __restrict__ V = static_cast<const float*>(p.v);
     float* __restrict__ O = static_cast<float*>(p.o);
     float* __restrict__ LSE = p.lse;
-    const int M = p.M, N = p.N;
     const float c_log2 = p.c_log2;
     __shared__ __attribute__((aligned(16))) float sK[2][T::kKElems];
     __shared__ __attribute__((aligned(16))) float sV[2][T::kVElems];
@@ -867,18 +955,19 @@ fa2_fwd_f32_kernel(const FwdParams p) {
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
-    const WgTask task = wg_task<CAUSAL, SPLIT>(p, T::kBM, BN);
-    const int bh = task.bh;
+    const WgTask task = wg_task<MASK, SPLIT>(p, T::kBM, BN);
+    const int M = task.sv.M, N = task.sv.N;
     const int qw0 = task.qt * T::kBM + wave * 32;
+    const int qw1 = min(qw0 + 32, M) - 1;
 
-    const float* Qh = Q + (int64_t)bh * M * D;
-    const float* Kh = K + (int64_t)task.bkv * N * D;
-    const float* Vh = V + (int64_t)task.bkv * N * D;
+    const float* Qh = Q + task.sv.q_row0 * D;
+    const float* Kh = K + task.sv.kv_row0 * D;
+    const float* Vh = V + task.sv.kv_row0 * D;
 
     // local tile kt is K/V tile kv_t0 + kt of the head
     const int kv_t0 = task.t_begin;
     const int n_kv = task.n_kv;
-    const int n_kv_wave = wave_tiles<CAUSAL>(p, task, qw0, 32, BN);
+    const WaveRange wtiles = wave_tiles<MASK>(p, task, qw0, 32, BN);
 
     // Q: lane half h holds d in [h*D/2, (h+1)*D/2) of its query row; MFMA step s
     // contracts d = h*D/2 + s in both operands.
@@ -934,7 +1023,7 @@ fa2_fwd_f32_kernel(const FwdParams p) {
         const bool has_next = kt + 1 < n_kv;
         if (has_next) load_tile(kt + 1);
 
-        if (kt < n_kv_wave) {
+        if (kt >= wtiles.first && kt < wtiles.end) {
             const float* kt_lds = sK[buf];
             const float* vt_lds = sV[buf];
 
@@ -954,16 +1043,15 @@ fa2_fwd_f32_kernel(const FwdParams p) {
             }
 
             const int kbase = (kv_t0 + kt) * BN;
-            const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > qw0);
-            if (need_mask) {
+            if (tile_needs_mask<MASK>(p, kbase, BN, N, qw0, qw1)) {
                 const int query = qw0 + l32;
+                const int hi = key_hi<MASK>(p, query, N), lo = key_lo<MASK>(p, query);
 #pragma unroll
                 for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kbase + 32 * kb + acc_row(r, h);
-                        const bool vis = key < N && (!CAUSAL || key <= query);
-                        if (!vis) sacc[kb][r] = -INFINITY;
+                        if (key > hi || key < lo) sacc[kb][r] = -INFINITY;
                     }
             }
 
@@ -1011,8 +1099,8 @@ fa2_fwd_f32_kernel(const FwdParams p) {
     if (query < M) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         // split K/V: the partial result goes to the workspace (also fp32)
-        float* orow = SPLIT ? partial_row(p, task, query, D) : O + ((int64_t)bh * M + query) * D;
-        float* lrow = SPLIT ? partial_l(p, task, query) : LSE + (int64_t)bh * M + query;
+        float* orow = SPLIT ? partial_row(p, task, query, D) : O + (task.sv.q_row0 + query) * D;
+        float* lrow = SPLIT ? partial_l(p, task, query) : LSE + task.sv.q_row0 + query;
 #pragma unroll
         for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
@@ -1095,18 +1183,18 @@ struct Entry {
 const Entry kTable[] = {
     // bf16, fp16: 8 waves (two per SIMD) share each K/V tile; 256 query rows per
     // workgroup; 64-key tiles at D=128, 128-key tiles at D=64 (measured best)
-    {FA2_DTYPE_BF16, 64, 0, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 64, 128, 8, 1, 2, false), 512, 256, 128, 1},
-    {FA2_DTYPE_BF16, 64, 1, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 64, 128, 8, 1, 2, true), 512, 256, 128, 1},
+    {FA2_DTYPE_BF16, 64, 0, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 64, 128, 8, 1, 2, kMaskNone), 512, 256, 128, 1},
+    {FA2_DTYPE_BF16, 64, 1, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 64, 128, 8, 1, 2, kMaskCausal), 512, 256, 128, 1},
     {FA2_DTYPE_BF16, 128, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 128, 64, false), 512, 256, 64, 1},
     {FA2_DTYPE_BF16, 128, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 128, 64, true), 512, 256, 64, 1},
-    {FA2_DTYPE_F16, 64, 0, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 64, 128, 8, 1, 2, false), 512, 256, 128, 1},
-    {FA2_DTYPE_F16, 64, 1, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 64, 128, 8, 1, 2, true), 512, 256, 128, 1},
+    {FA2_DTYPE_F16, 64, 0, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 64, 128, 8, 1, 2, kMaskNone), 512, 256, 128, 1},
+    {FA2_DTYPE_F16, 64, 1, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 64, 128, 8, 1, 2, kMaskCausal), 512, 256, 128, 1},
     {FA2_DTYPE_F16, 128, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, false), 512, 256, 64, 1},
     {FA2_DTYPE_F16, 128, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, true), 512, 256, 64, 1},
-    {FA2_DTYPE_F32, 64, 0, FWD_PAIR(fa2_fwd_f32_kernel, 64, 64, 4, false), 256, 128, 64, 2},
-    {FA2_DTYPE_F32, 64, 1, FWD_PAIR(fa2_fwd_f32_kernel, 64, 64, 4, true), 256, 128, 64, 2},
-    {FA2_DTYPE_F32, 128, 0, FWD_PAIR(fa2_fwd_f32_kernel, 128, 32, 4, false), 256, 128, 32, 1},
-    {FA2_DTYPE_F32, 128, 1, FWD_PAIR(fa2_fwd_f32_kernel, 128, 32, 4, true), 256, 128, 32, 1},
+    {FA2_DTYPE_F32, 64, 0, FWD_PAIR(fa2_fwd_f32_kernel, 64, 64, 4, kMaskNone), 256, 128, 64, 2},
+    {FA2_DTYPE_F32, 64, 1, FWD_PAIR(fa2_fwd_f32_kernel, 64, 64, 4, kMaskCausal), 256, 128, 64, 2},
+    {FA2_DTYPE_F32, 128, 0, FWD_PAIR(fa2_fwd_f32_kernel, 128, 32, 4, kMaskNone), 256, 128, 32, 1},
+    {FA2_DTYPE_F32, 128, 1, FWD_PAIR(fa2_fwd_f32_kernel, 128, 32, 4, kMaskCausal), 256, 128, 32, 1},
 };
 #undef FWD_PAIR
 
@@ -1122,7 +1210,6 @@ const MergeEntry kMergeTable[] = {
     {FA2_DTYPE_F32, 64, FWD_KERNEL(fa2_merge_kernel<float, 64>)},
     {FA2_DTYPE_F32, 128, FWD_KERNEL(fa2_merge_kernel<float, 128>)},
 };
-#undef FWD_KERNEL
 
 constexpr int kCUs = 256;  // MI355X; the split heuristic's design point
 
@@ -1145,6 +1232,50 @@ int choose_splits(const Entry& e, int64_t BH, int64_t M, int64_t N) {
     s = std::min<int64_t>(s, FA2_MAX_SPLITS);
     return (int)std::max<int64_t>(1, s);
 }
+
+// Sliding-window and packed-sequence entry points: the general 8-wave 16-bit
+// kernel (also at D = 128, where the dense entry point uses the ping-pong
+// kernel) and the fp32 kernel, one instantiation per mask kind, unsplit.
+struct LocalEntry {
+    int dtype, D, mask;
+    const void* kernel;
+    int threads;
+    int block_m;  // query rows per workgroup
+};
+#define LOCAL_HALF(E, code, mask)                                                                      \
+    {code, 64, mask, FWD_KERNEL(fa2_fwd_half_kernel<E, 64, 128, 8, 1, 2, mask, false>), 512, 256},     \
+    {code, 128, mask, FWD_KERNEL(fa2_fwd_half_kernel<E, 128, 64, 8, 1, 2, mask, false>), 512, 256}
+#define LOCAL_F32(mask)                                                                                \
+    {FA2_DTYPE_F32, 64, mask, FWD_KERNEL(fa2_fwd_f32_kernel<64, 64, 4, mask, false>), 256, 128},        \
+    {FA2_DTYPE_F32, 128, mask, FWD_KERNEL(fa2_fwd_f32_kernel<128, 32, 4, mask, false>), 256, 128}
+const LocalEntry kLocalTable[] = {
+    LOCAL_HALF(__bf16, FA2_DTYPE_BF16, kMaskNone),  LOCAL_HALF(__bf16, FA2_DTYPE_BF16, kMaskCausal),
+    LOCAL_HALF(__bf16, FA2_DTYPE_BF16, kMaskLocal), LOCAL_HALF(_Float16, FA2_DTYPE_F16, kMaskNone),
+    LOCAL_HALF(_Float16, FA2_DTYPE_F16, kMaskCausal), LOCAL_HALF(_Float16, FA2_DTYPE_F16, kMaskLocal),
+    LOCAL_F32(kMaskNone), LOCAL_F32(kMaskCausal), LOCAL_F32(kMaskLocal),
+};
+#undef LOCAL_HALF
+#undef LOCAL_F32
+
+const LocalEntry* find_local_entry(int dtype, int64_t D, int mask) {
+    for (const LocalEntry& t : kLocalTable)
+        if (t.dtype == dtype && t.D == D && t.mask == mask) return &t;
+    return nullptr;
+}
+
+// Window sides as the kernels take them: causal is a right bound of 0; a
+// side that reaches past every row (left >= M, right >= N) is unbounded (-1),
+// which also keeps i - wl and i + wr inside int.  The mask kind follows.
+int normalise_window(int64_t& wl, int64_t& wr, int causal, int64_t M, int64_t N) {
+    if (causal) wr = 0;
+    if (wl >= M) wl = -1;
+    if (wr >= N) wr = -1;
+    if (wl < 0 && wr < 0) return kMaskNone;
+    if (wl < 0 && wr == 0) return kMaskCausal;
+    return kMaskLocal;
+}
+
+#undef FWD_KERNEL
 
 int64_t workspace_bytes(int64_t BH, int64_t M, int64_t D, int n_splits) {
     if (n_splits <= 1) return 0;
@@ -1229,9 +1360,11 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
 
     if (M == 0 || BH == 0) return FA2_OK;
 
-    FwdParams prm;
+    FwdParams prm{};  // dense layout, no window: cu_q = cu_k = null
     prm.q = q; prm.k = k; prm.v = v; prm.o = o; prm.lse = lse;
     prm.BH = (int)ks.BH; prm.H = (int)ks.H; prm.G = (int)ks.G;
+    prm.Hk = (int)(ks.H / ks.G);
+    prm.wl = prm.wr = -1;
     prm.M = (int)ks.M; prm.N = (int)N;
     prm.n_qt = (int)n_qt;
     prm.c_log2 = scale * 1.44269504088896340736f;  // scale * log2(e)
@@ -1268,6 +1401,114 @@ extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o, flo
                        float scale, int causal, int dtype, void* stream) {
     return fa2_fwd_ex(q, k, v, o, lse, B, H, H > 0 ? H : 1, M, N, D, scale, causal, dtype, 1, nullptr, 0,
                       stream);
+}
+
+extern "C" int fa2_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+                             float scale, int causal, int64_t window_left, int64_t window_right,
+                             int dtype, void* stream) {
+    // ---- argument checks, all before any HIP call
+    if (B < 0 || H < 0 || Hk < 1 || M < 0 || N <= 0 || D <= 0) return FA2_ERR_INVALID_ARGUMENT;
+    const bool q_rows = B > 0 && H > 0 && M > 0, kv_rows = B > 0;
+    if ((q_rows && (!q || !o || !lse)) || (kv_rows && (!k || !v))) return FA2_ERR_INVALID_ARGUMENT;
+    if (H > 0 && (Hk > H || H % Hk != 0)) return FA2_ERR_INVALID_ARGUMENT;
+    if (dtype != FA2_DTYPE_F32 && dtype != FA2_DTYPE_BF16 && dtype != FA2_DTYPE_F16) return FA2_ERR_INVALID_ARGUMENT;
+    if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARGUMENT;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA2_ERR_INVALID_ARGUMENT;
+    if (window_left < -1 || window_right < -1) return FA2_ERR_INVALID_ARGUMENT;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4))
+        return FA2_ERR_INVALID_ARGUMENT;
+    if (D != 64 && D != 128) return FA2_ERR_UNSUPPORTED;
+    const int64_t kMax = (int64_t)1 << 31;
+    if (B > kMax || H > kMax || M >= kMax || N >= kMax) return FA2_ERR_UNSUPPORTED;
+    const int64_t BH = B * H;
+    const size_t elt = dtype == FA2_DTYPE_F32 ? 4 : 2;
+    if (M * D * (int64_t)elt >= kMax || N * D * (int64_t)elt >= kMax || BH >= kMax) return FA2_ERR_UNSUPPORTED;
+    const size_t o_bytes = (size_t)BH * M * D * elt;
+    const size_t kv_bytes = (size_t)B * Hk * N * D * elt;
+    const size_t lse_bytes = (size_t)BH * M * 4;
+    if (overlaps(o, o_bytes, q, o_bytes) || overlaps(o, o_bytes, k, kv_bytes) ||
+        overlaps(o, o_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, q, o_bytes) ||
+        overlaps(lse, lse_bytes, k, kv_bytes) || overlaps(lse, lse_bytes, v, kv_bytes) ||
+        overlaps(lse, lse_bytes, o, o_bytes))
+        return FA2_ERR_INVALID_ARGUMENT;
+    int64_t wl = window_left, wr = window_right;
+    const int mask = normalise_window(wl, wr, causal, M, N);
+    const LocalEntry* e = find_local_entry(dtype, D, mask);
+    if (!e) return FA2_ERR_UNSUPPORTED;
+    const int64_t n_qt = ceil_div(M, e->block_m);
+    if (n_qt * BH >= kMax) return FA2_ERR_UNSUPPORTED;
+    if (M == 0 || BH == 0) return FA2_OK;
+
+    FwdParams prm{};
+    prm.q = q; prm.k = k; prm.v = v; prm.o = o; prm.lse = lse;
+    prm.BH = (int)BH; prm.H = (int)H; prm.Hk = (int)Hk; prm.G = (int)(H / Hk);
+    prm.M = (int)M; prm.N = (int)N;
+    prm.n_qt = (int)n_qt;
+    prm.tiles_per_split = (int)N;  // at least every tile
+    prm.wl = (int)wl; prm.wr = (int)wr;
+    prm.c_log2 = scale * kLog2e;
+    void* args[] = {&prm};
+    const hipError_t err = hipLaunchKernel(e->kernel, dim3((unsigned)(n_qt * BH)), dim3(e->threads), args, 0,
+                                           static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+extern "C" int fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int64_t B, int64_t H, int64_t Hk, int64_t total_q, int64_t total_k,
+                              int64_t max_seqlen_q, int64_t D, float scale, int causal,
+                              int64_t window_left, int64_t window_right, int dtype, void* stream) {
+    // ---- argument checks, all before any HIP call
+    if (B < 0 || H < 0 || Hk < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || D <= 0)
+        return FA2_ERR_INVALID_ARGUMENT;
+    if (max_seqlen_q > total_q) return FA2_ERR_INVALID_ARGUMENT;
+    if (B > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return FA2_ERR_INVALID_ARGUMENT;
+    if ((H > 0 && total_q > 0 && (!q || !o || !lse)) || (total_k > 0 && (!k || !v))) return FA2_ERR_INVALID_ARGUMENT;
+    if (H > 0 && (Hk > H || H % Hk != 0)) return FA2_ERR_INVALID_ARGUMENT;
+    if (dtype != FA2_DTYPE_F32 && dtype != FA2_DTYPE_BF16 && dtype != FA2_DTYPE_F16) return FA2_ERR_INVALID_ARGUMENT;
+    if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARGUMENT;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA2_ERR_INVALID_ARGUMENT;
+    if (window_left < -1 || window_right < -1) return FA2_ERR_INVALID_ARGUMENT;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4) ||
+        misaligned(cu_seqlens_q, 4) || misaligned(cu_seqlens_k, 4))
+        return FA2_ERR_INVALID_ARGUMENT;
+    if (D != 64 && D != 128) return FA2_ERR_UNSUPPORTED;
+    const int64_t kMax = (int64_t)1 << 31;
+    const size_t elt = dtype == FA2_DTYPE_F32 ? 4 : 2;
+    if (B >= kMax || H >= kMax || Hk >= kMax || total_q * D * (int64_t)elt >= kMax ||
+        total_k * D * (int64_t)elt >= kMax)
+        return FA2_ERR_UNSUPPORTED;
+    const size_t o_bytes = (size_t)H * total_q * D * elt;
+    const size_t kv_bytes = (size_t)Hk * total_k * D * elt;
+    const size_t lse_bytes = (size_t)H * total_q * 4;
+    if (overlaps(o, o_bytes, q, o_bytes) || overlaps(o, o_bytes, k, kv_bytes) ||
+        overlaps(o, o_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, q, o_bytes) ||
+        overlaps(lse, lse_bytes, k, kv_bytes) || overlaps(lse, lse_bytes, v, kv_bytes) ||
+        overlaps(lse, lse_bytes, o, o_bytes))
+        return FA2_ERR_INVALID_ARGUMENT;
+    int64_t wl = window_left, wr = window_right;
+    const int mask = normalise_window(wl, wr, causal, total_q, total_k);
+    const LocalEntry* e = find_local_entry(dtype, D, mask);
+    if (!e) return FA2_ERR_UNSUPPORTED;
+    const int64_t BH = B * H;
+    const int64_t n_qt = ceil_div(max_seqlen_q, e->block_m);
+    if (BH >= kMax || n_qt * BH >= kMax) return FA2_ERR_UNSUPPORTED;
+    if (BH == 0 || n_qt == 0) return FA2_OK;
+
+    FwdParams prm{};
+    prm.q = q; prm.k = k; prm.v = v; prm.o = o; prm.lse = lse;
+    prm.cu_q = cu_seqlens_q; prm.cu_k = cu_seqlens_k;
+    prm.total_q = (int)total_q; prm.total_k = (int)total_k;
+    prm.BH = (int)BH; prm.H = (int)H; prm.Hk = (int)Hk; prm.G = (int)(H / Hk);
+    prm.n_qt = (int)n_qt;
+    prm.tiles_per_split = (int)total_k + 1;  // at least every tile
+    prm.wl = (int)wl; prm.wr = (int)wr;
+    prm.c_log2 = scale * kLog2e;
+    void* args[] = {&prm};
+    const hipError_t err = hipLaunchKernel(e->kernel, dim3((unsigned)(n_qt * BH)), dim3(e->threads), args, 0,
+                                           static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
 extern "C" const char* fa2_status_string(int status) {

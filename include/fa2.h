@@ -159,6 +159,69 @@ int fa2_fwd_num_splits(int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, i
                        int dtype);
 
 /*
+ * fa2_fwd_local -- fa2_fwd_ex (unsplit) with a sliding-window mask, the
+ * window_size = (left, right) option of the pages' Python entry point ("From
+ * FlashAttention to FlashAttention 2", section "Layer 1"; "Writing
+ * FlashAttention 2 in Triton", its list of next steps: a sliding-window
+ * variant of the causal mask formula).
+ *
+ * Query row i sees key j iff
+ *   (window_left  == -1 or j >= i - window_left) and
+ *   (window_right == -1 or j <= i + window_right) and
+ *   (!causal or j <= i),
+ * measured from the top-left diagonal j = i like the causal mask (causal is
+ * window_right = 0).  window_left, window_right >= -1; -1 leaves that side
+ * unbounded, so (-1, -1) is plain fa2_fwd_ex attention.  A row that sees no
+ * key (possible once a window is set, e.g. M > N with a finite left side)
+ * gets o = 0 and lse = -inf.
+ *
+ * Layout, other arguments, ownership and errors as for fa2_fwd_ex with
+ * n_splits = 1 (k, v are [B, Hk, N, D]); dtype F32, BF16 or F16; D = 64 or
+ * 128.  One kernel is enqueued on `stream`.
+ */
+int fa2_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+                  float scale, int causal, int64_t window_left, int64_t window_right,
+                  int dtype, void* stream);
+
+/*
+ * fa2_fwd_varlen -- the forward pass over a batch of sequences of different
+ * lengths packed without padding, the cu_seqlens interface of the pages'
+ * variable-length entry point ("From FlashAttention to FlashAttention 2",
+ * section "Layer 1": cu_seqlens_q / cu_seqlens_k for packed batching).
+ *
+ * Layout (head-major packing; each head's rows of all sequences are
+ * contiguous, sequence after sequence):
+ *   q, o   [H,  total_q, D]   element type `dtype`
+ *   k, v   [Hk, total_k, D]   element type `dtype`
+ *   lse    [H,  total_q]      float32
+ *   cu_seqlens_q, cu_seqlens_k  int32 device arrays of B + 1 offsets:
+ *          sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *          and keys cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of every head;
+ *          offsets start at 0, never decrease and end at total_q (total_k).
+ * Each sequence attends only to its own keys, with the causal / window
+ * rules of fa2_fwd_local applied to its own row and key indices (query head
+ * h reads K/V head h / (H / Hk)).  A sequence without keys gets o = 0 and
+ * lse = -inf.
+ *
+ * max_seqlen_q: an upper bound of every sequence's query count (it sizes the
+ * grid; rows of a longer sequence past it are not computed); 0 <=
+ * max_seqlen_q <= total_q.
+ *
+ * The offsets live in device memory and are not read by the host: offsets
+ * outside [0, total] or decreasing are clamped by the kernel (a sequence
+ * then covers fewer rows or none), so they cannot make it address memory
+ * outside q, k, v, o or lse, but the result for such a batch is
+ * unspecified.  Other checks and errors as for fa2_fwd_local; B == 0, H ==
+ * 0 or max_seqlen_q == 0 launches nothing.  One kernel on `stream`.
+ */
+int fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                   int64_t B, int64_t H, int64_t Hk, int64_t total_q, int64_t total_k,
+                   int64_t max_seqlen_q, int64_t D, float scale, int causal,
+                   int64_t window_left, int64_t window_right, int dtype, void* stream);
+
+/*
  * fa2_bwd -- gradients of the attention forward pass on one HIP stream.
  *
  * For the forward O = softmax(S) V with S = scale * Q K^T (optionally causal,

@@ -254,3 +254,46 @@ def test_null_pointers_allowed_for_empty_buffers():
     assert call(k=0, M=0) == fa2.FA2_ERR_INVALID_ARGUMENT
     assert call_bwd(q=0, o=0, lse=0, do=0, dq=0, delta=0, M=0) != fa2.FA2_ERR_INVALID_ARGUMENT
     assert call_bwd(dk=0, M=0) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+# ------------------------------------------- fa2_fwd_local / fa2_fwd_varlen (no launches)
+
+def call_local(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Hk=2, M=16, N=16, D=64, causal=0, wl=4, wr=4, dtype=None):
+    dtype = fa2.FA2_DTYPE_BF16 if dtype is None else dtype
+    return fa2.fa2_fwd_local(q, k, v, o, lse, B, H, Hk, M, N, D, 0.125, causal, wl, wr, dtype, None)
+
+
+CQ, CK = 11 * A, 12 * A
+
+
+def call_varlen(q=Q, k=K, v=V, o=O, lse=L, cq=CQ, ck=CK, B=2, H=2, Hk=2, total_q=16, total_k=16, max_q=8,
+                D=64, causal=0, wl=-1, wr=-1, dtype=None):
+    dtype = fa2.FA2_DTYPE_BF16 if dtype is None else dtype
+    return fa2.fa2_fwd_varlen(q, k, v, o, lse, cq, ck, B, H, Hk, total_q, total_k, max_q, D, 0.125, causal,
+                              wl, wr, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [dict(wl=-2), dict(wr=-5), dict(q=0), dict(k=0), dict(N=0), dict(Hk=3),
+                                dict(causal=2), dict(o=Q), dict(lse=O + 4), dict(q=Q + 8)])
+def test_local_bad_arguments_rejected(kw):
+    assert call_local(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+def test_local_unsupported_and_empty():
+    assert call_local(D=96) == fa2.FA2_ERR_UNSUPPORTED
+    assert call_local(M=0) == fa2.FA2_OK
+    assert call_local(B=0) == fa2.FA2_OK
+
+
+@pytest.mark.parametrize("kw", [dict(cq=0), dict(ck=0), dict(cq=CQ + 2), dict(max_q=17), dict(max_q=-1),
+                                dict(total_k=-1), dict(wl=-3), dict(q=0), dict(o=K), dict(H=4, Hk=3)])
+def test_varlen_bad_arguments_rejected(kw):
+    assert call_varlen(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+def test_varlen_unsupported_and_empty():
+    assert call_varlen(D=32) == fa2.FA2_ERR_UNSUPPORTED
+    # nothing to launch: no sequences, no heads, or no query rows anywhere
+    assert call_varlen(B=0, cq=0, ck=0) == fa2.FA2_OK
+    assert call_varlen(H=0) == fa2.FA2_OK
+    assert call_varlen(max_q=0) == fa2.FA2_OK
