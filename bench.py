@@ -84,10 +84,13 @@ def load_traffic(workload: str):
 
 def dominant_kernel(w, splits: int = 1) -> str:
     """The forward kernel the library launches for this workload (its
-    dispatch table: fp32 kernel, or the 16-bit kernel, ping-pong at D=128),
-    followed by the combine kernel when the key range is split."""
+    dispatch table: fp32 kernel, or the 16-bit kernel, ping-pong at D=128
+    on the dense unwindowed path), followed by the combine kernel when the
+    key range is split."""
     if w.dtype == "f32":
         k = "fa2_fwd_f32_kernel"
+    elif w.lengths is not None or w.window != (-1, -1):
+        k = "fa2_fwd_half_kernel"
     else:
         k = "fa2_fwd_half_pp_kernel" if w.D == 128 else "fa2_fwd_half_kernel"
     return k + (f" x{splits} splits + fa2_merge_kernel" if splits > 1 else "")
@@ -277,6 +280,10 @@ def main(argv=None):
     def setup(w):
         q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
         o = torch.empty_like(q)
+        if w.lengths is not None:
+            # packed sequences: lse [H, total]; the "workspace" slot carries the offsets
+            lse = torch.empty((w.H, q.shape[1]), dtype=torch.float32, device=dev)
+            return q, k, v, o, lse, workloads.cu_seqlens(w).to(dev), 1
         lse = torch.empty((w.B, w.H, w.M), dtype=torch.float32, device=dev)
         splits = splits_of(w)
         need = fa2.fa2_fwd_workspace_bytes(w.B, w.H, w.M, w.D, splits)
@@ -286,7 +293,18 @@ def main(argv=None):
     def launcher(w, bufs):
         q, k, v, o, lse, ws, splits = bufs
         code = code_of(w)
-        if w.Hk is None and splits == 1:
+        if w.lengths is not None:
+            total = q.shape[1]
+            args_ = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                     ws.data_ptr(), w.B, w.H, w.kv_heads, total, total, max(w.lengths), w.D, w.scale,
+                     int(w.causal), w.window[0], w.window[1], code, stream.cuda_stream)
+            call = fa2.fa2_fwd_varlen
+        elif w.window != (-1, -1):
+            args_ = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, w.kv_heads, w.M, w.N, w.D, w.scale, int(w.causal), w.window[0], w.window[1],
+                     code, stream.cuda_stream)
+            call = fa2.fa2_fwd_local
+        elif w.Hk is None and splits == 1:
             # the plain entry point
             args_ = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                      w.B, w.H, w.M, w.N, w.D, w.scale, int(w.causal), code, stream.cuda_stream)
@@ -407,7 +425,12 @@ def main(argv=None):
             us, us_cold = median(hot) * 1e3, median(cold) * 1e3
             tf = wx.flops / (us * 1e-6) / 1e12
             bound, ach, pk, unit = roofline_of(wx, us * 1e-6)
-            table[name] = {"shape": f"B={wx.B},H={wx.H},Hk={wx.kv_heads},M={wx.M},N={wx.N},D={wx.D}",
+            shape = f"B={wx.B},H={wx.H},Hk={wx.kv_heads},M={wx.M},N={wx.N},D={wx.D}"
+            if wx.window != (-1, -1):
+                shape += f",window={wx.window}"
+            if wx.lengths is not None:
+                shape += f",packed lengths={list(wx.lengths)}"
+            table[name] = {"shape": shape,
                            "dtype": wx.dtype, "causal": wx.causal, "kv_splits": bx[6],
                            "us_median": round(us, 2), "us_median_l2_flushed": round(us_cold, 2),
                            "tflops": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK_TFLOPS[wx.dtype], 4),

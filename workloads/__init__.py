@@ -25,7 +25,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "ORDER", "WIDENED", "BACKWARD", "get", "make_inputs", "make_dout", "torch_dtype"]
+__all__ = ["Workload", "WORKLOADS", "ORDER", "WIDENED", "BACKWARD", "get", "make_inputs", "make_dout", "torch_dtype",
+           "visible_pairs", "workload_inputs", "cu_seqlens"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -47,6 +48,12 @@ class Workload:
     Hk: Optional[int] = None
     # K/V splits the bench asks for (0 = the library's choice, 1 = unsplit)
     n_splits: int = 1
+    # sliding window (left, right); -1 leaves a side unbounded
+    window: tuple = (-1, -1)
+    # packed variable-length batch: per-sequence lengths (queries = keys);
+    # None = the dense [B, H, M, D] layout.  With lengths, B is their count and
+    # M, N are the longest one.
+    lengths: Optional[tuple] = None
 
     @property
     def kv_heads(self) -> int:
@@ -62,10 +69,17 @@ class Workload:
 
         This is the accounting of the bench harness in "FlashAttention-2 from
         PyTorch to Triton" (two matmuls of M*N*D multiply-adds, halved for
-        causal), generalised to M != N.
+        causal), generalised to M != N.  With a sliding window or packed
+        sequences the M*N (or M*N/2) term becomes the number of visible
+        (query, key) pairs.
         """
-        f = 4.0 * self.B * self.H * self.M * self.N * self.D
-        return f / 2 if self.causal else f
+        if self.window == (-1, -1) and self.lengths is None:
+            f = 4.0 * self.B * self.H * self.M * self.N * self.D
+            return f / 2 if self.causal else f
+        lens = self.lengths if self.lengths is not None else (self.M,) * self.B
+        kl = self.lengths if self.lengths is not None else (self.N,) * self.B
+        pairs = sum(visible_pairs(m, n, self.causal, *self.window) for m, n in zip(lens, kl))
+        return 4.0 * self.H * self.D * pairs
 
     @property
     def bwd_flops(self) -> float:
@@ -81,6 +95,9 @@ class Workload:
     @property
     def compulsory_bytes(self) -> int:
         """Read Q, K, V once and write O and the fp32 logsumexp once."""
+        if self.lengths is not None:
+            total = sum(self.lengths)
+            return ((self.H * 2 + self.kv_heads * 2) * total * self.D) * self.elt_bytes + 4 * self.H * total
         bh = self.B * self.H
         kv = self.B * self.kv_heads * 2 * self.N * self.D
         return (bh * 2 * self.M * self.D + kv) * self.elt_bytes + 4 * bh * self.M
@@ -89,6 +106,28 @@ class Workload:
         hk = "" if self.Hk is None else f",Hk={self.Hk}"
         return (f"{self.name}: B={self.B},H={self.H}{hk},M={self.M},N={self.N},D={self.D},"
                 f"{self.dtype},{'causal' if self.causal else 'non-causal'}")
+
+
+def visible_pairs(M: int, N: int, causal: bool, wl: int = -1, wr: int = -1) -> int:
+    """Number of (query, key) pairs a query row i < M and key j < N form
+    when j must satisfy i - wl <= j <= i + wr (a side is unbounded when -1)
+    and j <= i when causal -- the rows' visible key counts, summed."""
+    import numpy as np
+    i = np.arange(M, dtype=np.int64)
+    lo = np.zeros(M, dtype=np.int64) if wl < 0 else np.maximum(0, i - wl)
+    hi = np.full(M, N - 1, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, i)
+    if wr >= 0:
+        hi = np.minimum(hi, i + wr)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def _varlen_lengths(count: int, lo: int, hi: int, seed: int) -> tuple:
+    """Seeded sequence lengths, uniform in [lo, hi]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return tuple(int(x) for x in torch.randint(lo, hi + 1, (count,), generator=g))
 
 
 WORKLOADS = {
@@ -120,7 +159,20 @@ WORKLOADS.update({
     "decode_gqa_bf16": Workload("decode_gqa_bf16", 4, 32, 16, 16384, 128, "bf16", False, seed=8,
                                 Hk=8, n_splits=0),
 })
-WIDENED = ["causal_f16_4k", "gqa_bf16_4k", "decode_gqa_bf16"]
+WORKLOADS.update({
+    # the long-context causal shape with a 4096-key sliding window (each row
+    # sees itself and the 4095 keys before it)
+    "swa_bf16_16k": Workload("swa_bf16_16k", 1, 32, 16384, 16384, 128, "bf16", True, seed=9,
+                             window=(4095, 0)),
+})
+_VL = _varlen_lengths(16, 128, 8192, seed=10)
+WORKLOADS.update({
+    # 16 packed causal sequences of 128..8192 tokens (seeded lengths), 4
+    # query heads per K/V head
+    "varlen_bf16_mix": Workload("varlen_bf16_mix", len(_VL), 16, max(_VL), max(_VL), 128, "bf16", True,
+                                seed=10, Hk=4, lengths=_VL),
+})
+WIDENED = ["causal_f16_4k", "gqa_bf16_4k", "decode_gqa_bf16", "swa_bf16_16k", "varlen_bf16_mix"]
 
 # Workloads whose backward pass the bench also times (16-bit only: the
 # backward has no fp32 kernels).
@@ -157,7 +209,19 @@ def make_inputs(B: int, H: int, M: int, N: int, D: int, dtype: str = "f32", seed
 
 
 def workload_inputs(w: Workload):
+    """(q, k, v) of a workload: dense [B,H,M,D] / [B,Hk,N,D], or for packed
+    sequences [H, total, D] / [Hk, total, D] drawn as one long sequence."""
+    if w.lengths is not None:
+        total = sum(w.lengths)
+        q, k, v = make_inputs(1, w.H, total, total, w.D, w.dtype, w.seed, w.qk_sigma, w.v_sigma, Hk=w.Hk)
+        return q[0], k[0], v[0]
     return make_inputs(w.B, w.H, w.M, w.N, w.D, w.dtype, w.seed, w.qk_sigma, w.v_sigma, Hk=w.Hk)
+
+
+def cu_seqlens(w: Workload):
+    """int32 offsets [B + 1] of a packed workload's sequences."""
+    import itertools
+    return torch.tensor([0] + list(itertools.accumulate(w.lengths)), dtype=torch.int32)
 
 
 def sample_rows(w: Workload, seed_offset: int = 1000):
