@@ -71,17 +71,38 @@ def test_workload_parity(name):
 
 @pytest.mark.parametrize("name", workloads.WIDENED)
 def test_widened_workload_parity(name):
-    # grouped-query heads, fp16 and split K/V at measured sizes
+    # grouped-query heads, fp16, split K/V, sliding window and packed
+    # sequences at the measured sizes, through the entry point the bench uses
     import exact_attention_23_amd as fa2
     w = workloads.get(name)
-    note("case " + w.describe() + f" n_splits={w.n_splits}")
+    note("case " + w.describe() + f" n_splits={w.n_splits} window={w.window}")
     q, k, v = workloads.workload_inputs(w)
-    o, lse = fa2.forward(q.cuda(), k.cuda(), v.cuda(), causal=w.causal, n_splits=w.n_splits)
+    if w.lengths is not None:
+        cu = workloads.cu_seqlens(w)
+        o, lse = fa2.forward_varlen(q.cuda(), k.cuda(), v.cuda(), cu.cuda(), cu.cuda(), max(w.lengths),
+                                    causal=w.causal, window=w.window)
+    else:
+        o, lse = fa2.forward(q.cuda(), k.cuda(), v.cuda(), causal=w.causal, n_splits=w.n_splits, window=w.window)
     torch.cuda.synchronize()
     o = o.float().cpu().numpy().astype(np.float64)
     lse = lse.cpu().numpy().astype(np.float64)
+    if w.lengths is not None:
+        # each sequence against the dense oracle on its own rows: all rows of
+        # short sequences, a seeded sample (first and last included) of long ones
+        g = np.random.default_rng(w.seed)
+        G = w.H // w.kv_heads
+        for b, (q0, q1) in enumerate(zip(cu[:-1].tolist(), cu[1:].tolist())):
+            n = q1 - q0
+            rows = np.arange(n) if n <= 256 else np.unique(np.r_[0, n - 1, g.choice(n, 62, replace=False)])
+            kb = np.repeat(k[:, q0:q1][None].float().numpy(), G, axis=1)
+            vb = np.repeat(v[:, q0:q1][None].float().numpy(), G, axis=1)
+            o_ref, l_ref = oracle.attention(q[None, :, q0:q1], kb, vb, w.scale, w.causal, rows=rows,
+                                            window=w.window)
+            compare(o[None, :, q0 + rows], lse[None, :, q0 + rows], o_ref, l_ref, w.dtype, f"{name} sequence {b}")
+        return
     rows = workloads.sample_rows(w)
-    o_ref, l_ref = oracle.attention(q, k, v, w.scale, w.causal, rows=None if rows is None else rows.numpy())
+    o_ref, l_ref = oracle.attention(q, k, v, w.scale, w.causal, rows=None if rows is None else rows.numpy(),
+                                    window=w.window)
     if rows is not None:
         o, lse = o[:, :, rows.numpy()], lse[:, :, rows.numpy()]
     compare(o, lse, o_ref, l_ref, w.dtype, name)

@@ -163,7 +163,7 @@ WORKLOADS.update({
     # the long-context causal shape with a 4096-key sliding window (each row
     # sees itself and the 4095 keys before it)
     "swa_bf16_16k": Workload("swa_bf16_16k", 1, 32, 16384, 16384, 128, "bf16", True, seed=9,
-                             window=(4095, 0)),
+                             window=(4095, 0), sample_rows=512),
 })
 _VL = _varlen_lengths(16, 128, 8192, seed=10)
 WORKLOADS.update({
