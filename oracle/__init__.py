@@ -66,6 +66,13 @@ def _bind(lib):
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_double, ctypes.c_int, ctypes.c_int,
     ]
+    lib.fa2_oracle_bwd_local.restype = ctypes.c_int
+    lib.fa2_oracle_bwd_local.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+    ]
     lib.fa2_oracle_max_threads.restype = ctypes.c_int
     lib.fa2_oracle_max_threads.argtypes = []
     return lib
@@ -152,6 +159,28 @@ def attention(q, k, v, scale: float, causal: bool, rows: Optional[np.ndarray] = 
     return o, lse
 
 
+def attention_bwd_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool,
+                         window=(-1, -1), threads: int = 0):
+    """Reference gradients over packed sequences (layout of
+    ``attention_varlen``): each sequence's rows through ``attention_bwd``
+    (no arithmetic here).  Returns (dq [H,total_q,D], dk, dv [Hk,total_k,D])
+    in float64; keys of no sequence keep a zero gradient."""
+    qa, ka, va, da = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q).tolist()]
+    ck = [int(x) for x in np.asarray(cu_seqlens_k).tolist()]
+    dq = np.zeros(qa.shape, dtype=np.float64)
+    dk = np.zeros(ka.shape, dtype=np.float64)
+    dv = np.zeros(va.shape, dtype=np.float64)
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 <= q0 or k1 <= k0:
+            continue
+        g = attention_bwd(qa[None, :, q0:q1], ka[None, :, k0:k1], va[None, :, k0:k1], da[None, :, q0:q1],
+                          scale, causal, threads=threads, window=window)
+        dq[:, q0:q1], dk[:, k0:k1], dv[:, k0:k1] = g[0][0], g[1][0], g[2][0]
+    return dq, dk, dv
+
+
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool,
                      window=(-1, -1), threads: int = 0):
     """Reference forward over packed variable-length sequences.
@@ -184,11 +213,13 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
     return o, lse
 
 
-def attention_bwd(q, k, v, dout, scale: float, causal: bool, threads: int = 0, _lib_override=None):
+def attention_bwd(q, k, v, dout, scale: float, causal: bool, threads: int = 0, _lib_override=None,
+                  window=(-1, -1)):
     """Reference gradients of the attention forward for the upstream gradient
     dout: q, dout [B,H,M,D]; k, v [B,Hk,N,D].  Returns (dq, dk, dv) as float64
     numpy arrays shaped like q, k, v; dk and dv sum over the query heads of
-    each K/V head."""
+    each K/V head.  ``window``: the forward's sliding window (see
+    ``attention``); rows that see no key have no gradient."""
     qa, ka, va, da = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
     B, H, M, D = qa.shape
     Hk, N = ka.shape[1], ka.shape[2]
@@ -199,9 +230,15 @@ def attention_bwd(q, k, v, dout, scale: float, causal: bool, threads: int = 0, _
     dk = np.empty((B, Hk, N, D), dtype=np.float64)
     dv = np.empty((B, Hk, N, D), dtype=np.float64)
     lib = _load() if _lib_override is None else _lib_override
-    rc = lib.fa2_oracle_bwd_gqa(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data,
-                                dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
-                                B, H, Hk, M, N, D, float(scale), int(bool(causal)), int(threads))
+    wl, wr = int(window[0]), int(window[1])
+    if wl >= 0 or wr >= 0:
+        rc = lib.fa2_oracle_bwd_local(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data,
+                                      dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                      B, H, Hk, M, N, D, float(scale), int(bool(causal)), wl, wr, int(threads))
+    else:
+        rc = lib.fa2_oracle_bwd_gqa(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data,
+                                    dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                    B, H, Hk, M, N, D, float(scale), int(bool(causal)), int(threads))
     if rc != 0:
         raise ValueError(f"fa2_oracle_bwd_gqa failed with status {rc}")
     return dq, dk, dv

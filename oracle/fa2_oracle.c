@@ -221,6 +221,8 @@ int fa2_oracle_fwd(const float* q, const float* k, const float* v, double* o,
  *   dQ[i]    = scale * sum_{j in J} dS_ij * K[j]                       (11)
  *   dK[j]   += scale * dS_ij * Q[i]                                    (12)
  *
+ * J is the forward's visible set (1), sliding window included; a row with an
+ * empty J has no gradient (dQ = 0, nothing added to dK, dV).
  * dK and dV of a K/V head sum over every query head that reads it (hk).
  * Sources: "From FlashAttention to FlashAttention 2", section "Layer 7: The
  * Backward Kernel" (steps 3-7 of its inner loop: dP = dO V^T, dS = P o (dP -
@@ -232,10 +234,15 @@ int fa2_oracle_fwd(const float* q, const float* k, const float* v, double* o,
  */
 static void oracle_bwd_row(const float* qi, const float* doi, const float* kbh,
                            const float* vbh, double* dqi, double* dkbh,
-                           double* dvbh, int64_t i, int64_t N, int64_t D,
-                           double scale, int causal, double* p, double* dp) {
-    const int64_t n_vis = causal ? (i + 1 < N ? i + 1 : N) : N;
-    /* P_ij, steps (1)-(4) of the forward */
+                           double* dvbh, int64_t j0, int64_t n_vis, int64_t D,
+                           double scale, double* p, double* dp) {
+    for (int64_t d = 0; d < D; ++d) dqi[d] = 0.0;
+    if (n_vis <= 0) return; /* a row that sees no key has no gradient */
+    kbh += j0 * D;
+    vbh += j0 * D;
+    dkbh += j0 * D;
+    dvbh += j0 * D;
+    /* P_ij, steps (2)-(4) of the forward over the visible keys */
     double m = -INFINITY;
     for (int64_t j = 0; j < n_vis; ++j) {
         const float* kj = kbh + j * D;
@@ -260,7 +267,6 @@ static void oracle_bwd_row(const float* qi, const float* doi, const float* kbh,
         Di += p[j] * dot;
     }
     /* (7), (10), (11), (12) */
-    for (int64_t d = 0; d < D; ++d) dqi[d] = 0.0;
     for (int64_t j = 0; j < n_vis; ++j) {
         const double ds = p[j] * (dp[j] - Di);
         const float* kj = kbh + j * D;
@@ -280,10 +286,11 @@ static void oracle_bwd_row(const float* qi, const float* doi, const float* kbh,
  * owns its K/V head's dk, dv), so no two threads add into the same row.
  * Returns 0 on success.
  */
-int fa2_oracle_bwd_gqa(const float* q, const float* k, const float* v,
-                       const float* dout, double* dq, double* dk, double* dv,
-                       int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N,
-                       int64_t D, double scale, int causal, int n_threads) {
+int fa2_oracle_bwd_local(const float* q, const float* k, const float* v,
+                         const float* dout, double* dq, double* dk, double* dv,
+                         int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N,
+                         int64_t D, double scale, int causal, int64_t wl, int64_t wr,
+                         int n_threads) {
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return FA2_ORACLE_EINVAL;
     if (B < 0 || H < 0 || M < 0 || N <= 0 || D <= 0) return FA2_ORACLE_EINVAL;
     if (Hk < 1 || H % Hk != 0) return FA2_ORACLE_EINVAL;
@@ -314,15 +321,27 @@ int fa2_oracle_bwd_gqa(const float* q, const float* k, const float* v,
             const float* vbh = v + bk * N * D;
             for (int64_t g = 0; g < group; ++g) {
                 const int64_t bh = b * H + hk * group + g; /* (hk) */
-                for (int64_t i = 0; i < M; ++i)
+                for (int64_t i = 0; i < M; ++i) {
+                    int64_t j0, n_vis;
+                    visible_keys(i, N, causal, wl, wr, &j0, &n_vis); /* (1) */
                     oracle_bwd_row(q + (bh * M + i) * D, dout + (bh * M + i) * D,
                                    kbh, vbh, dq + (bh * M + i) * D,
-                                   dk + bk * N * D, dv + bk * N * D, i, N, D,
-                                   scale, causal, p, dp);
+                                   dk + bk * N * D, dv + bk * N * D, j0, n_vis, D,
+                                   scale, p, dp);
+                }
             }
         }
         free(p);
         free(dp);
     }
     return status;
+}
+
+/* No sliding window. */
+int fa2_oracle_bwd_gqa(const float* q, const float* k, const float* v,
+                       const float* dout, double* dq, double* dk, double* dv,
+                       int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N,
+                       int64_t D, double scale, int causal, int n_threads) {
+    return fa2_oracle_bwd_local(q, k, v, dout, dq, dk, dv, B, H, Hk, M, N, D, scale,
+                                causal, -1, -1, n_threads);
 }

@@ -47,17 +47,17 @@ def close(a, b, atol, rtol=0.0):
 
 # ------------------------------------------------------------ finite differences
 
-def check_finite_differences(bwd, causal, H=2, Hk=1, M=9, N=11, D=8, seed=0):
+def check_finite_differences(bwd, causal, H=2, Hk=1, M=9, N=11, D=8, seed=0, window=(-1, -1)):
     """d/dx sum(O * dO) by central differences of the fp64 forward, at a few
     entries of each of q, k and v."""
     q, k, v = grid_rnd((1, H, M, D), seed), grid_rnd((1, Hk, N, D), seed + 1), grid_rnd((1, Hk, N, D), seed + 2)
     do = rnd((1, H, M, D), seed + 3)
     scale = 0.3
-    dq, dk, dv = bwd(q, k, v, do, scale, causal)
+    dq, dk, dv = bwd(q, k, v, do, scale, causal, window=window)
     h = 2.0 ** -12
 
     def loss(qq, kk, vv):
-        o, _ = oracle.attention(qq, kk, vv, scale, causal)
+        o, _ = oracle.attention(qq, kk, vv, scale, causal, window=window)
         return float(np.sum(o * do.astype(np.float64)))
 
     g = np.random.default_rng(seed + 4)
@@ -76,7 +76,23 @@ def check_finite_differences(bwd, causal, H=2, Hk=1, M=9, N=11, D=8, seed=0):
 
 # --------------------------------------------------------------- library case
 
-def torch_grads(q, k, v, do, scale, causal):
+def band_mask(M, N, causal, wl, wr):
+    """Boolean [M, N] mask of the visible pairs, written out from the
+    statement of the window (key j visible to row i iff i - wl <= j <= i + wr,
+    a side unbounded when -1, and j <= i when causal)."""
+    i = torch.arange(M)[:, None]
+    j = torch.arange(N)[None, :]
+    mask = torch.ones(M, N, dtype=torch.bool)
+    if causal:
+        mask &= j <= i
+    if wl >= 0:
+        mask &= j >= i - wl
+    if wr >= 0:
+        mask &= j <= i + wr
+    return mask
+
+
+def torch_grads(q, k, v, do, scale, causal, window=(-1, -1)):
     """fp64 autograd through a materialised, masked softmax; GQA by repeating
     K/V heads (autograd sums the repeated heads' gradients)."""
     H, Hk = q.shape[1], k.shape[1]
@@ -84,9 +100,9 @@ def torch_grads(q, k, v, do, scale, causal):
     kk = tk.repeat_interleave(H // Hk, dim=1)
     vv = tv.repeat_interleave(H // Hk, dim=1)
     s = scale * torch.matmul(tq, kk.transpose(-1, -2))
-    if causal:
+    if causal or window != (-1, -1):
         M, N = q.shape[2], k.shape[2]
-        mask = torch.ones(M, N, dtype=torch.bool).tril()
+        mask = band_mask(M, N, causal, *window)
         s = s.masked_fill(~mask, float("-inf"))
     o = torch.matmul(torch.softmax(s, dim=-1), vv)
     o.backward(torch.from_numpy(do.astype(np.float64)))
@@ -101,12 +117,12 @@ LIB_CASES = [  # (B, H, Hk, M, N, D)
 ]
 
 
-def check_torch(bwd, B, H, Hk, M, N, D, causal, seed=10):
+def check_torch(bwd, B, H, Hk, M, N, D, causal, seed=10, window=(-1, -1)):
     q, k, v = rnd((B, H, M, D), seed), rnd((B, Hk, N, D), seed + 1), rnd((B, Hk, N, D), seed + 2)
     do = rnd((B, H, M, D), seed + 3)
     scale = 1 / math.sqrt(D)
-    got = bwd(q, k, v, do, scale, causal)
-    ref = torch_grads(q, k, v, do, scale, causal)
+    got = bwd(q, k, v, do, scale, causal, window=window)
+    ref = torch_grads(q, k, v, do, scale, causal, window)
     for g, r in zip(got, ref):
         close(g, r, 1e-12, 1e-10)
 
@@ -186,8 +202,25 @@ def check_invariants(bwd, causal, seed=30):
     close(vdv, odo, 1e-12)
 
 
-def bwd_oracle(q, k, v, do, scale, causal):
-    return oracle.attention_bwd(q, k, v, do, scale, causal)
+def check_window_empty_rows(bwd):
+    # M > N with a left window of 2: rows 13.. see no key.  They have no
+    # gradient (dQ = 0) and their dO adds nothing to dK, dV: the gradients
+    # equal those of the problem without those rows.
+    M, N, D = 20, 11, 8
+    q, k, v, do = rnd((1, 2, M, D), 50), rnd((1, 2, N, D), 51), rnd((1, 2, N, D), 52), rnd((1, 2, M, D), 53)
+    dq, dk, dv = bwd(q, k, v, do, 0.3, False, window=(2, -1))
+    close(dq[:, :, 13:], 0.0, 0)
+    dq2, dk2, dv2 = bwd(q[:, :, :13].copy(), k, v, do[:, :, :13].copy(), 0.3, False, window=(2, -1))
+    close(dq[:, :, :13], dq2, 1e-15)
+    close(dk, dk2, 1e-15)
+    close(dv, dv2, 1e-15)
+
+
+WINDOW_CASES = [((3, 2), False), ((4, -1), True), ((-1, 3), False), ((0, 0), False)]
+
+
+def bwd_oracle(q, k, v, do, scale, causal, window=(-1, -1)):
+    return oracle.attention_bwd(q, k, v, do, scale, causal, window=window)
 
 
 ALL_PINS = (
@@ -196,6 +229,9 @@ ALL_PINS = (
     + [lambda b, c=c: check_finite_differences(b, c) for c in (False, True)]
     + [lambda b, c=c: check_finite_differences(b, c, H=4, Hk=2, M=12, N=7, seed=5) for c in (False, True)]
     + [lambda b, s=s, c=c: check_torch(b, *s, c) for s in LIB_CASES for c in (False, True)]
+    + [check_window_empty_rows]
+    + [lambda b, w=w, c=c: check_finite_differences(b, c, M=12, N=14, seed=7, window=w) for w, c in WINDOW_CASES]
+    + [lambda b, w=w, c=c: check_torch(b, 1, 4, 2, 26, 30, 16, c, window=w) for w, c in WINDOW_CASES]
 )
 
 
@@ -227,6 +263,43 @@ def test_finite_differences(causal, heads):
 @pytest.mark.parametrize("shape", LIB_CASES, ids=lambda s: "x".join(map(str, s)))
 def test_matches_torch_autograd(shape, causal):
     check_torch(bwd_oracle, *shape, causal)
+
+
+def test_window_empty_rows_have_no_gradient():
+    check_window_empty_rows(bwd_oracle)
+
+
+@pytest.mark.parametrize("window,causal", WINDOW_CASES)
+def test_window_finite_differences(window, causal):
+    check_finite_differences(bwd_oracle, causal, H=4, Hk=2, M=12, N=14, seed=7, window=window)
+
+
+@pytest.mark.parametrize("window,causal", WINDOW_CASES)
+def test_window_matches_torch_autograd(window, causal):
+    check_torch(bwd_oracle, 1, 4, 2, 26, 30, 16, causal, window=window)
+
+
+def test_varlen_backward_equals_per_sequence():
+    # packed sequences: each sequence's gradients are the dense oracle's on
+    # its own rows; keys of a sequence without queries get zero gradient
+    lens_q, lens_k = [6, 0, 13, 9], [8, 5, 13, 0]
+    cq, ck = np.cumsum([0] + lens_q), np.cumsum([0] + lens_k)
+    q, do = rnd((4, cq[-1], 16), 60), rnd((4, cq[-1], 16), 61)
+    k, v = rnd((2, ck[-1], 16), 62), rnd((2, ck[-1], 16), 63)
+    for causal, window in [(False, (-1, -1)), (True, (-1, -1)), (False, (3, 1))]:
+        dq, dk, dv = oracle.attention_bwd_varlen(q, k, v, do, cq, ck, 0.25, causal, window)
+        for b in range(4):
+            q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+            if q1 == q0 or k1 == k0:
+                close(dq[:, q0:q1], 0.0, 0)
+                close(dk[:, k0:k1], 0.0, 0)
+                close(dv[:, k0:k1], 0.0, 0)
+                continue
+            g = oracle.attention_bwd(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], do[None, :, q0:q1],
+                                     0.25, causal, window=window)
+            np.testing.assert_array_equal(dq[:, q0:q1], g[0][0])
+            np.testing.assert_array_equal(dk[:, k0:k1], g[1][0])
+            np.testing.assert_array_equal(dv[:, k0:k1], g[2][0])
 
 
 def test_bf16_inputs_are_widened_exactly():
@@ -263,10 +336,14 @@ MUTANTS = {
     "dV weighted by dS": ("dvj[d] += p[j] * (double)doi[d];", "dvj[d] += ds * (double)doi[d];"),
     "bwd weights unnormalised": ("for (int64_t j = 0; j < n_vis; ++j) p[j] /= l;",
                                  "for (int64_t j = 0; j < n_vis; ++j) p[j] /= 1.0;"),
-    "bwd causal reversed": ("const int64_t n_vis = causal ? (i + 1 < N ? i + 1 : N) : N;",
-                            "const int64_t n_vis = !causal ? (i + 1 < N ? i + 1 : N) : N;"),
-    "bwd diagonal excluded": ("const int64_t n_vis = causal ? (i + 1 < N ? i + 1 : N) : N;",
-                              "const int64_t n_vis = causal ? (i < N ? (i > 0 ? i : 1) : N) : N;"),
+    "causal reversed": ("if (causal && i < hi) hi = i;", "if (causal && i > lo) lo = i;"),
+    "diagonal excluded": ("if (causal && i < hi) hi = i;", "if (causal && i - 1 < hi) hi = i - 1;"),
+    "bwd window ignored": ("visible_keys(i, N, causal, wl, wr, &j0, &n_vis); /* (1) */",
+                           "visible_keys(i, N, causal, -1, -1, &j0, &n_vis); /* (1) */"),
+    "bwd empty row keeps a gradient": ("if (n_vis <= 0) return; /* a row that sees no key has no gradient */",
+                                       "if (n_vis <= 0) { n_vis = 1; j0 = 0; }"),
+    "bwd visible keys misplaced": ("    kbh += j0 * D;\n    vbh += j0 * D;\n    dkbh += j0 * D;",
+                                   "    kbh += j0 * D;\n    vbh += j0 * D;\n    dkbh += 0 * D;"),
     "bwd kv head misindexed": ("const int64_t bh = b * H + hk * group + g;",
                                "const int64_t bh = b * H + g * Hk + hk;"),
     "dP reads K": ("const float* vrow = vbh + j * D;", "const float* vrow = kbh + j * D;"),
@@ -290,8 +367,8 @@ def _build_mutant(tmp_path, name, edit):
 def test_bwd_pins_catch_planted_mistakes(tmp_path, name):
     lib = _build_mutant(tmp_path, name, MUTANTS[name])
 
-    def mutant(q, k, v, do, scale, causal):
-        return oracle.attention_bwd(q, k, v, do, scale, causal, _lib_override=lib)
+    def mutant(q, k, v, do, scale, causal, window=(-1, -1)):
+        return oracle.attention_bwd(q, k, v, do, scale, causal, _lib_override=lib, window=window)
 
     failures = 0
     for pin in ALL_PINS:
