@@ -6,11 +6,12 @@ There is no CPU fallback: if the library is missing, importing the binding
 raises.
 
 ``fa2_fwd``, ``fa2_fwd_ex``, ``fa2_fwd_workspace_bytes``,
-``fa2_fwd_num_splits``, ``fa2_fwd_local``, ``fa2_fwd_varlen`` and ``fa2_bwd``
-mirror the C entry points of ``include/fa2.h`` one to one (raw device
-pointers and sizes).  ``forward``, ``forward_varlen`` and ``backward`` are the
-tensor-level conveniences that allocate outputs (and any split-K/V
-workspace) with torch and call the library on the current stream;
+``fa2_fwd_num_splits``, ``fa2_fwd_local``, ``fa2_fwd_varlen``, ``fa2_bwd``,
+``fa2_bwd_local`` and ``fa2_bwd_varlen`` mirror the C entry points of
+``include/fa2.h`` one to one (raw device pointers and sizes).  ``forward``,
+``forward_varlen``, ``backward`` and ``backward_varlen`` are the tensor-level
+conveniences that allocate outputs (and any split-K/V workspace) with torch
+and call the library on the current stream;
 ``attention`` wraps forward and backward in a ``torch.autograd.Function``.
 """
 from __future__ import annotations
@@ -22,8 +23,8 @@ import os
 __all__ = ["FA2_DTYPE_F32", "FA2_DTYPE_BF16", "FA2_DTYPE_F16", "FA2_OK", "FA2_ERR_INVALID_ARGUMENT",
            "FA2_ERR_UNSUPPORTED", "FA2_ERR_LAUNCH", "FA2_ERR_NO_DEVICE", "FA2_MAX_SPLITS", "Fa2Error",
            "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_workspace_bytes", "fa2_fwd_num_splits", "fa2_fwd_local",
-           "fa2_fwd_varlen", "fa2_bwd", "fa2_status_string", "forward", "forward_varlen", "backward",
-           "attention", "library_path", "EXPORTED_SYMBOLS"]
+           "fa2_fwd_varlen", "fa2_bwd", "fa2_bwd_local", "fa2_bwd_varlen", "fa2_status_string", "forward",
+           "forward_varlen", "backward", "backward_varlen", "attention", "library_path", "EXPORTED_SYMBOLS"]
 
 FA2_DTYPE_F32 = 0
 FA2_DTYPE_BF16 = 1
@@ -37,8 +38,8 @@ FA2_ERR_NO_DEVICE = 4
 
 FA2_MAX_SPLITS = 128
 
-EXPORTED_SYMBOLS = ("fa2_bwd", "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_local", "fa2_fwd_num_splits",
-                    "fa2_fwd_varlen", "fa2_fwd_workspace_bytes", "fa2_status_string")
+EXPORTED_SYMBOLS = ("fa2_bwd", "fa2_bwd_local", "fa2_bwd_varlen", "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_local",
+                    "fa2_fwd_num_splits", "fa2_fwd_varlen", "fa2_fwd_workspace_bytes", "fa2_status_string")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa2.so")
@@ -103,6 +104,12 @@ def _load():
     lib.fa2_bwd.restype = ctypes.c_int
     lib.fa2_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa2_bwd_local.restype = ctypes.c_int
+    lib.fa2_bwd_local.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.fa2_bwd_varlen.restype = ctypes.c_int
+    lib.fa2_bwd_varlen.argtypes = [ctypes.c_void_p] * 12 + [ctypes.c_int64] * 8 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -166,6 +173,24 @@ def fa2_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: in
     Returns the fa2_status code."""
     return int(_lib.fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hk, M, N, D, scale, causal,
                             dtype, stream))
+
+
+def fa2_bwd_local(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, delta: int,
+                  B: int, H: int, Hk: int, M: int, N: int, D: int, scale: float, causal: int, window_left: int,
+                  window_right: int, dtype: int, stream: int | None) -> int:
+    """Direct call of the sliding-window backward C entry point."""
+    return int(_lib.fa2_bwd_local(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hk, M, N, D, scale, causal,
+                                  window_left, window_right, dtype, stream))
+
+
+def fa2_bwd_varlen(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, delta: int,
+                   cu_seqlens_q: int, cu_seqlens_k: int, B: int, H: int, Hk: int, total_q: int, total_k: int,
+                   max_seqlen_q: int, max_seqlen_k: int, D: int, scale: float, causal: int, window_left: int,
+                   window_right: int, dtype: int, stream: int | None) -> int:
+    """Direct call of the packed-sequence backward C entry point."""
+    return int(_lib.fa2_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, delta, cu_seqlens_q, cu_seqlens_k, B, H,
+                                   Hk, total_q, total_k, max_seqlen_q, max_seqlen_k, D, scale, causal,
+                                   window_left, window_right, dtype, stream))
 
 
 def fa2_status_string(status: int) -> str:
@@ -296,7 +321,7 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causa
 
 
 def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
-             dq=None, dk=None, dv=None, delta=None):
+             dq=None, dk=None, dv=None, delta=None, window=(-1, -1)):
     """Gradients of the attention forward on the current CUDA/HIP stream.
 
     q, o, dout: [B,H,M,D]; k, v: [B,Hk,N,D], contiguous device tensors of one
@@ -304,7 +329,8 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     for the same inputs, scale and causal flag.  Returns (dq, dk, dv), shaped
     and typed like q, k, v; dk and dv sum over the query heads of each K/V
     head.  ``delta`` ([B,H,M] float32, rowsum(dout * o)) is scratch the call
-    writes; it is allocated with torch unless given.
+    writes; it is allocated with torch unless given.  ``window``: the
+    sliding window the forward used (fa2_bwd_local).
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
@@ -340,9 +366,48 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
         raise ValueError("delta must be a contiguous float32 tensor of shape [B,H,M]")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        st = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                     B, H, Hk, M, N, D, float(scale), int(bool(causal)), _dtype_code(q), stream)
+        st = fa2_bwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                           B, H, Hk, M, N, D, float(scale), int(bool(causal)), int(window[0]), int(window[1]),
+                           _dtype_code(q), stream)
+    if st != FA2_OK:
+        raise Fa2Error(st)
+    return dq, dk, dv
+
+
+def backward_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    causal: bool = False, scale: float | None = None, window=(-1, -1)):
+    """Gradients of forward_varlen: q, o, dout [H, total_q, D]; k, v
+    [Hk, total_k, D]; lse [H, total_q] from forward_varlen with the same
+    offsets, causal flag, window and scale.  Returns (dq, dk, dv)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 3-D device tensor [heads, total, D]")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, o and dout must share one dtype")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32 or t.dim() != 1
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous 1-D int32 device tensor")
+    H, total_q, D = q.shape
+    Hk, total_k = k.shape[0], k.shape[1]
+    if (k.shape != (Hk, total_k, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape
+            or Hk < 1 or H % Hk or cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1):
+        raise ValueError("shape mismatch between q, k, v, o, dout and the offsets")
+    if lse.shape != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [H, total_q]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa2_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1, H, Hk,
+                            total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D, float(scale),
+                            int(bool(causal)), int(window[0]), int(window[1]), _dtype_code(q), stream)
     if st != FA2_OK:
         raise Fa2Error(st)
     return dq, dk, dv
@@ -353,17 +418,18 @@ def _make_function():
 
     class _Attention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, causal, scale):
-            o, lse = forward(q, k, v, causal=causal, scale=scale)
+        def forward(ctx, q, k, v, causal, scale, window):
+            o, lse = forward(q, k, v, causal=causal, scale=scale, window=window)
             ctx.save_for_backward(q, k, v, o, lse)
-            ctx.causal, ctx.scale = causal, scale
+            ctx.causal, ctx.scale, ctx.window = causal, scale, window
             return o
 
         @staticmethod
         def backward(ctx, dout):
             q, k, v, o, lse = ctx.saved_tensors
-            dq, dk, dv = backward(q, k, v, o, lse, dout.contiguous(), causal=ctx.causal, scale=ctx.scale)
-            return dq, dk, dv, None, None
+            dq, dk, dv = backward(q, k, v, o, lse, dout.contiguous(), causal=ctx.causal, scale=ctx.scale,
+                                  window=ctx.window)
+            return dq, dk, dv, None, None, None
 
     return _Attention
 
@@ -371,12 +437,13 @@ def _make_function():
 _function = None
 
 
-def attention(q, k, v, causal: bool = False, scale: float | None = None):
-    """softmax(scale * q k^T) v with autograd: the forward runs fa2_fwd_ex,
-    the backward fa2_bwd (bfloat16 / float16 inputs for the backward)."""
+def attention(q, k, v, causal: bool = False, scale: float | None = None, window=(-1, -1)):
+    """softmax(scale * q k^T) v with autograd: the forward runs fa2_fwd_ex
+    (fa2_fwd_local with a window), the backward fa2_bwd_local (bfloat16 /
+    float16 inputs for the backward)."""
     global _function
     if _function is None:
         _function = _make_function()
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    return _function.apply(q, k, v, bool(causal), float(scale))
+    return _function.apply(q, k, v, bool(causal), float(scale), (int(window[0]), int(window[1])))

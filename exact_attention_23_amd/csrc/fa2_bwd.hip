@@ -48,6 +48,7 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include <algorithm>
@@ -67,14 +68,94 @@ struct BwdParams {
     void* dq;
     void* dk;
     void* dv;
+    const int* cu_q;    // packed sequences: query row offsets [B + 1] (device), else null
+    const int* cu_k;    // packed sequences: key row offsets [B + 1]
+    int total_q, total_k;  // packed sequences: rows per head of q (o, dout, lse, delta) and of k (v)
     int BH;     // batch * query heads, as the kernels see them
     int BHk;    // batch * K/V heads
+    int H, Hk;  // query and K/V heads, as the kernels see them
     int G;      // query heads per K/V head, as the kernels see them (0: none)
-    int M, N;   // query rows per head (kernel view), keys per head
+    int M, N;   // dense: query rows per head (kernel view), keys per head
     int n_qt;   // query tiles per head, of the kernel's own tile height
+    int wl, wr; // sliding window: keys i - wl .. i + wr (-1: unbounded side)
     float c_log2;  // scale * log2(e)
     float scale;
 };
+
+// The sequence of batch b: the whole head in the dense layout (cu_q null),
+// else rows cu_q[b] .. cu_q[b + 1] - 1 (keys cu_k[b] .. cu_k[b + 1] - 1) of
+// each head of the packed layout, clamped into [0, total].
+struct BwdSeq {
+    int q0, k0;  // first query / key row of the sequence inside a head's rows
+    int M, N;    // its query rows and keys
+};
+__device__ __forceinline__ BwdSeq bwd_seq(const BwdParams& p, int b) {
+    BwdSeq s;
+    if (p.cu_q == nullptr) {
+        s.q0 = s.k0 = 0;
+        s.M = p.M;
+        s.N = p.N;
+        return s;
+    }
+    const int q0 = min(max(p.cu_q[b], 0), p.total_q), q1 = min(max(p.cu_q[b + 1], q0), p.total_q);
+    const int k0 = min(max(p.cu_k[b], 0), p.total_k), k1 = min(max(p.cu_k[b + 1], k0), p.total_k);
+    s.q0 = q0;
+    s.k0 = k0;
+    s.M = q1 - q0;
+    s.N = k1 - k0;
+    return s;
+}
+// Row (of D elements) of q, o, dout, dq, lse, delta holding query row 0 of
+// head bh's sequence, and of k, v, dk, dv holding key row 0 of K/V head bkv's.
+__device__ __forceinline__ int64_t q_row0(const BwdParams& p, const BwdSeq& s, int bh) {
+    return p.cu_q ? (int64_t)(bh % p.H) * p.total_q + s.q0 : (int64_t)bh * p.M;
+}
+__device__ __forceinline__ int64_t kv_row0(const BwdParams& p, const BwdSeq& s, int bkv) {
+    return p.cu_q ? (int64_t)(bkv % p.Hk) * p.total_k + s.k0 : (int64_t)bkv * p.N;
+}
+
+// The stored logsumexp of a row in log2 units, as the exponent offset of
+// P = exp2(S c - L2).  A row that saw no key (L = -inf: possible under a
+// window, or for a packed sequence without keys) has no gradient; +inf makes
+// its P exactly 0 whatever its (masked, -inf) scores, where -inf would give
+// exp2(-inf + inf) = NaN.  Rows past M pass +inf too.
+__device__ __forceinline__ float l2_of(float lse) {
+    return lse == -INFINITY ? INFINITY : lse * kLog2e;
+}
+
+// Query tiles [lo, hi) of height BQ whose rows see some key in [ka, kb] of a
+// sequence of M rows.
+template <int MASK>
+__device__ __forceinline__ void query_tiles(const BwdParams& p, int ka, int kb, int M, int BQ, int& lo, int& hi) {
+    lo = hi = 0;
+    if (ka > kb || M <= 0) return;
+    const int i_lo = query_lo<MASK>(p.wr, ka), i_hi = query_hi<MASK>(p.wl, kb, M);
+    if (i_lo > i_hi) return;
+    lo = i_lo / BQ;
+    hi = i_hi / BQ + 1;
+}
+// Do query rows r0 .. r0 + 31 and keys k0 .. k0 + 31 see each other at all
+// (live), and does every row see every key (full; keys past N do not matter
+// to the dK/dV kernels, which never store them).
+template <int MASK>
+__device__ __forceinline__ bool block_live(const BwdParams& p, int r0, int k0, int M, int N) {
+    if (r0 >= M || k0 >= N) return false;
+    return r0 <= query_hi<MASK>(p.wl, min(k0 + 31, N - 1), M) && r0 + 31 >= query_lo<MASK>(p.wr, k0);
+}
+template <int MASK>
+__device__ __forceinline__ bool block_full(const BwdParams& p, int r0, int k0) {
+    return key_lo<MASK>(p.wl, r0 + 31) <= k0 && key_hi<MASK>(p.wr, r0, INT_MAX) >= k0 + 31;
+}
+// Mask the S accumulator of rows rb + acc_row(r, h) (rb = the block's first
+// row) against this lane's key.
+template <int MASK>
+__device__ __forceinline__ void mask_rows(const BwdParams& p, floatx16& sacc, int rb, int h, int key) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int q = rb + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key > key_hi<MASK>(p.wr, q, INT_MAX) || key < key_lo<MASK>(p.wl, q)) sacc[r] = -INFINITY;
+    }
+}
 
 // 16-byte chunk XOR of LDS row r for tiles that are read both row-wise (A
 // operand, 32 rows at one chunk: a quarter-wave covers 16 rows) and
@@ -191,7 +272,7 @@ struct BwdKVTraits {
     static_assert(BQ * (D / 8) % (64 * NW) == 0, "loader split");
 };
 
-template <typename E, int D, int BQ, int NW, int WAVES_PER_SIMD, bool CAUSAL>
+template <typename E, int D, int BQ, int NW, int WAVES_PER_SIMD, int MASK>
 __global__ void __launch_bounds__(NW * 64, WAVES_PER_SIMD)
 fa2_bwd_dkdv_kernel(const BwdParams p) {
     using T = BwdKVTraits<D, BQ, NW>;
@@ -202,7 +283,6 @@ fa2_bwd_dkdv_kernel(const BwdParams p) {
     const E* __restrict__ dO = static_cast<const E*>(p.dout);
     E* __restrict__ dK = static_cast<E*>(p.dk);
     E* __restrict__ dV = static_cast<E*>(p.dv);
-    const int M = p.M, N = p.N;
     const float c_log2 = p.c_log2;
     // double-buffered Q and dO tiles, and the tile's L (log2 units) and Delta
     __shared__ __attribute__((aligned(1024))) char sQ0[T::kTileBytes];
@@ -221,13 +301,16 @@ fa2_bwd_dkdv_kernel(const BwdParams p) {
     // query tiles), K/V heads fastest
     const int bkv = blockIdx.x % p.BHk;
     const int kt = blockIdx.x / p.BHk;
+    const BwdSeq sq = bwd_seq(p, p.cu_q ? bkv / p.Hk : 0);
+    const int M = sq.M, N = sq.N;
     const int kbase = kt * T::kBN;
     const int k0 = kbase + 32 * wave;  // first key of this wave
     const int key = k0 + l32;          // this lane's key
 
     // K and V rows of the wave's keys: B operands of S = Q K^T and dP = dO V^T
-    const E* Kh = K + (int64_t)bkv * N * D;
-    const E* Vh = V + (int64_t)bkv * N * D;
+    const int64_t kvr = kv_row0(p, sq, bkv);
+    const E* Kh = K + kvr * D;
+    const E* Vh = V + kvr * D;
     V8 kf[T::kDS], vf[T::kDS];
 #pragma unroll
     for (int s = 0; s < T::kDS; ++s) {
@@ -240,10 +323,11 @@ fa2_bwd_dkdv_kernel(const BwdParams p) {
         }
     }
 
-    // query tiles: every query head of the group, from the first tile that
-    // reaches the workgroup's first key (causal) to the end
-    const int qt0 = CAUSAL ? min(kbase / BQ, p.n_qt) : 0;
-    const int per_g = p.n_qt - qt0;
+    // query tiles: every query head of the group, the tiles whose rows see
+    // some key of the workgroup
+    int qt0, qt1;
+    query_tiles<MASK>(p, kbase, min(kbase + T::kBN, N) - 1, M, BQ, qt0, qt1);
+    const int per_g = qt1 - qt0;
     const int n_it = p.G * per_g;
 
     floatx16 dkacc[T::kDB], dvacc[T::kDB];
@@ -264,18 +348,20 @@ fa2_bwd_dkdv_kernel(const BwdParams p) {
     auto issue_tile = [&](int it, char* qdst, char* odst) {
         int bh, qt;
         tile_head(it, bh, qt);
-        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BQ>(Q + (int64_t)bh * M * D, cp_off, wave_u, qt, M, qdst);
-        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BQ>(dO + (int64_t)bh * M * D, cp_off, wave_u, qt, M, odst);
+        const int64_t qr = q_row0(p, sq, bh);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BQ>(Q + qr * D, cp_off, wave_u, qt, M, qdst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BQ>(dO + qr * D, cp_off, wave_u, qt, M, odst);
     };
-    // wave 0 fetches the tile's L (times log2 e; +inf past M, so those rows
-    // get P = 0), wave 1 its Delta (0 past M)
+    // wave 0 fetches the tile's L (log2 units, l2_of), wave 1 its Delta
+    // (0 past M)
     auto fetch_ld = [&](int it) -> float {
         int bh, qt;
         tile_head(it, bh, qt);
         const int row = qt * BQ + lane;
         if (lane >= BQ || wave > 1) return 0.f;
-        if (wave == 0) return row < M ? p.lse[(int64_t)bh * M + row] * kLog2e : INFINITY;
-        return row < M ? p.delta[(int64_t)bh * M + row] : 0.f;
+        const int64_t qr = q_row0(p, sq, bh);
+        if (wave == 0) return l2_of(row < M ? p.lse[qr + row] : INFINITY);
+        return row < M ? p.delta[qr + row] : 0.f;
     };
     auto store_ld = [&](float x, float* sl, float* sd) {
         if (lane < BQ) {
@@ -288,9 +374,11 @@ fa2_bwd_dkdv_kernel(const BwdParams p) {
         int bh, qt;
         tile_head(it, bh, qt);
         const int row0 = qt * BQ;
-        // nothing to do for keys past N, or (causal) when every query of the
-        // tile precedes every key of the wave
-        if (k0 >= N || (CAUSAL && row0 + BQ - 1 < k0)) return;
+        // nothing to do unless some row of the tile sees some key of the wave
+        bool live = false;
+#pragma unroll
+        for (int qb = 0; qb < T::kQB; ++qb) live = live || block_live<MASK>(p, row0 + 32 * qb, k0, M, N);
+        if (!live) return;
         // S = Q K^T and dP = dO V^T (rows: queries, columns: the wave's keys)
         floatx16 sacc[T::kQB], pacc[T::kQB];
 #pragma unroll
@@ -312,7 +400,9 @@ fa2_bwd_dkdv_kernel(const BwdParams p) {
         // P = exp2(S c - L2) and dS = P (dP - Delta), rounded once to 16 bits
         // as B operands of the dV and dK products; register r of the
         // accumulator holds query row0 + 32 qb + acc_row(r, h).
-        const bool diag = CAUSAL && row0 < k0 + 31;
+        bool full = true;  // every row of the tile sees every key of the wave
+#pragma unroll
+        for (int qb = 0; qb < T::kQB; ++qb) full = full && block_full<MASK>(p, row0 + 32 * qb, k0);
         uint32_t pw[T::kQB][2][4], sw[T::kQB][2][4];
 #pragma unroll
         for (int qb = 0; qb < T::kQB; ++qb) {
@@ -322,12 +412,9 @@ fa2_bwd_dkdv_kernel(const BwdParams p) {
                 l4[g] = *reinterpret_cast<const floatx4*>(ls + 32 * qb + 8 * g + 4 * h);
                 d4[g] = *reinterpret_cast<const floatx4*>(dls + 32 * qb + 8 * g + 4 * h);
             }
-            if (diag) {
+            if (MASK != kMaskNone && !full) {
                 __asm__ volatile("");  // keep this a branch, not a select per element
-                const int lim = row0 + 32 * qb + 4 * h - key;  // visible iff acc_row part >= -lim
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (8 * (r >> 2) + (r & 3) < -lim) sacc[qb][r] = -INFINITY;
+                mask_rows<MASK>(p, sacc[qb], row0 + 32 * qb, h, key);
             }
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
@@ -391,8 +478,8 @@ fa2_bwd_dkdv_kernel(const BwdParams p) {
     // ---- epilogue: dK = scale dS^T Q, dV = P^T dO, rounded to nearest even
     if (key < N) {
         const float scale = p.scale;
-        E* krow = dK + ((int64_t)bkv * N + key) * D;
-        E* vrow = dV + ((int64_t)bkv * N + key) * D;
+        E* krow = dK + (kvr + key) * D;
+        E* vrow = dV + (kvr + key) * D;
 #pragma unroll
         for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
@@ -442,7 +529,7 @@ struct BwdPairTraits {
     static_assert(kPartBytes <= kQTileBytes && 2 * kPartBytes <= kKTileBytes, "pair sum space");
 };
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, int MASK>
 __global__ void __launch_bounds__(512, 2)
 fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
     using T = BwdPairTraits<D>;
@@ -453,7 +540,6 @@ fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
     const E* __restrict__ dO = static_cast<const E*>(p.dout);
     E* __restrict__ dK = static_cast<E*>(p.dk);
     E* __restrict__ dV = static_cast<E*>(p.dv);
-    const int M = p.M, N = p.N;
     const float c_log2 = p.c_log2;
     __shared__ __attribute__((aligned(1024))) char sK[T::kKTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV[T::kKTileBytes];
@@ -475,12 +561,18 @@ fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
     // query tiles), K/V heads fastest
     const int bkv = blockIdx.x % p.BHk;
     const int kt = blockIdx.x / p.BHk;
+    const BwdSeq sq = bwd_seq(p, p.cu_q ? bkv / p.Hk : 0);
+    const int M = sq.M, N = sq.N;
+    const int64_t kvr = kv_row0(p, sq, bkv);
     const int kbase = kt * T::kBN;
     const int k0 = kbase + 32 * kb;  // first key of this wave
     const int key = k0 + l32;        // this lane's key
 
-    const int qt0 = CAUSAL ? min(kbase / T::kBQ, p.n_qt) : 0;
-    const int per_g = p.n_qt - qt0;
+    // query tiles: every query head of the group, the tiles whose rows see
+    // some key of the workgroup
+    int qt0, qt1;
+    query_tiles<MASK>(p, kbase, min(kbase + T::kBN, N) - 1, M, T::kBQ, qt0, qt1);
+    const int per_g = qt1 - qt0;
     const int n_it = p.G * per_g;
 
     floatx16 dkacc[T::kDB], dvacc[T::kDB];
@@ -504,18 +596,20 @@ fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
     auto issue_tile = [&](int it, char* qdst, char* odst) {
         int bh, qt;
         tile_head(it, bh, qt);
-        copy_tile_to_lds<T::kQLoads, T::kRowBytes, T::kBQ>(Q + (int64_t)bh * M * D, q_off, wave_u, qt, M, qdst);
-        copy_tile_to_lds<T::kQLoads, T::kRowBytes, T::kBQ>(dO + (int64_t)bh * M * D, q_off, wave_u, qt, M, odst);
+        const int64_t qr = q_row0(p, sq, bh);
+        copy_tile_to_lds<T::kQLoads, T::kRowBytes, T::kBQ>(Q + qr * D, q_off, wave_u, qt, M, qdst);
+        copy_tile_to_lds<T::kQLoads, T::kRowBytes, T::kBQ>(dO + qr * D, q_off, wave_u, qt, M, odst);
     };
-    // wave 0 fetches the tile's L (times log2 e; +inf past M, so those rows
-    // get P = 0), wave 1 its Delta (0 past M)
+    // wave 0 fetches the tile's L (log2 units, l2_of), wave 1 its Delta
+    // (0 past M)
     auto fetch_ld = [&](int it) -> float {
         int bh, qt;
         tile_head(it, bh, qt);
         const int row = qt * T::kBQ + lane;
         if (wave > 1) return 0.f;
-        if (wave == 0) return row < M ? p.lse[(int64_t)bh * M + row] * kLog2e : INFINITY;
-        return row < M ? p.delta[(int64_t)bh * M + row] : 0.f;
+        const int64_t qr = q_row0(p, sq, bh);
+        if (wave == 0) return l2_of(row < M ? p.lse[qr + row] : INFINITY);
+        return row < M ? p.delta[qr + row] : 0.f;
     };
     auto store_ld = [&](float x, float* sl, float* sd) {
         if (wave == 0) sl[lane] = x;
@@ -526,9 +620,8 @@ fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
         int bh, qt;
         tile_head(it, bh, qt);
         const int r0 = qt * T::kBQ + 32 * qb;  // first query row of the wave's block
-        // nothing to do for keys past N, rows past M, or (causal) when every
-        // row of the block precedes every key of the wave
-        if (k0 >= N || r0 >= M || (CAUSAL && r0 + 31 < k0)) return;
+        // nothing to do unless some row of the block sees some key of the wave
+        if (!block_live<MASK>(p, r0, k0, M, N)) return;
         // S = Q K^T and dP = dO V^T (rows: the block's queries, columns: the
         // wave's keys), K and V rows read from LDS as B operands
         floatx16 sacc = floatx16{}, pacc = floatx16{};
@@ -543,12 +636,9 @@ fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
         }
         // P = exp2(S c - L2), dS = P (dP - Delta); register r holds query
         // r0 + acc_row(r, h)
-        if (CAUSAL && r0 < k0 + 31) {
+        if (MASK != kMaskNone && !block_full<MASK>(p, r0, k0)) {
             __asm__ volatile("");  // keep this a branch, not a select per element
-            const int lim = r0 + 4 * h - key;  // visible iff the acc_row part >= -lim
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (8 * (r >> 2) + (r & 3) < -lim) sacc[r] = -INFINITY;
+            mask_rows<MASK>(p, sacc, r0, h, key);
         }
         uint32_t pw[2][4], sw[2][4];
 #pragma unroll
@@ -581,8 +671,8 @@ fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
 
     // ---- prologue: the workgroup's K and V tiles, the first Q/dO tile
     if (n_it > 0) {
-        copy_tile_to_lds<T::kKLoads, T::kRowBytes, T::kBN>(K + (int64_t)bkv * N * D, k_off, wave_u, kt, N, sK);
-        copy_tile_to_lds<T::kKLoads, T::kRowBytes, T::kBN>(V + (int64_t)bkv * N * D, k_off, wave_u, kt, N, sV);
+        copy_tile_to_lds<T::kKLoads, T::kRowBytes, T::kBN>(K + kvr * D, k_off, wave_u, kt, N, sK);
+        copy_tile_to_lds<T::kKLoads, T::kRowBytes, T::kBN>(V + kvr * D, k_off, wave_u, kt, N, sV);
         issue_tile(0, sQ0, sO0);
         store_ld(fetch_ld(0), sL0, sD0);
     }
@@ -632,8 +722,8 @@ fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
     // nearest even
     if (qb == 0 && key < N) {
         const float scale = p.scale;
-        E* krow = dK + ((int64_t)bkv * N + key) * D;
-        E* vrow = dV + ((int64_t)bkv * N + key) * D;
+        E* krow = dK + (kvr + key) * D;
+        E* vrow = dV + (kvr + key) * D;
 #pragma unroll
         for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
@@ -672,7 +762,7 @@ struct BwdQTraits {
     static_assert(BN * (D / 8) % (64 * NW) == 0, "loader split");
 };
 
-template <typename E, int D, int BN, int NW, int WAVES_PER_SIMD, bool CAUSAL>
+template <typename E, int D, int BN, int NW, int WAVES_PER_SIMD, int MASK>
 __global__ void __launch_bounds__(NW * 64, WAVES_PER_SIMD)
 fa2_bwd_dq_kernel(const BwdParams p) {
     using T = BwdQTraits<D, BN, NW>;
@@ -682,7 +772,6 @@ fa2_bwd_dq_kernel(const BwdParams p) {
     const E* __restrict__ V = static_cast<const E*>(p.v);
     const E* __restrict__ dO = static_cast<const E*>(p.dout);
     E* __restrict__ dQ = static_cast<E*>(p.dq);
-    const int M = p.M, N = p.N;
     const float c_log2 = p.c_log2;
     __shared__ __attribute__((aligned(1024))) char sK0[T::kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV0[T::kTileBytes];
@@ -698,15 +787,19 @@ fa2_bwd_dq_kernel(const BwdParams p) {
     // query tiles major (heaviest first under a causal mask), heads fastest
     const int bh = blockIdx.x % p.BH;
     int qt = blockIdx.x / p.BH;
-    if (CAUSAL) qt = p.n_qt - 1 - qt;
+    if (MASK == kMaskCausal) qt = p.n_qt - 1 - qt;
     const int bkv = p.G == 1 ? bh : bh / p.G;
+    const BwdSeq sq = bwd_seq(p, p.cu_q ? bh / p.H : 0);
+    const int M = sq.M, N = sq.N;
+    const int64_t qr = q_row0(p, sq, bh), kvr = kv_row0(p, sq, bkv);
     const int qw0 = qt * T::kBM + 32 * wave;  // first query row of this wave
+    const int qw1 = min(qw0 + 32, M) - 1;     // its last row
     const int query = qw0 + l32;              // this lane's query row
 
     // Q and dO rows of the lane's query: B operands of S^T = K Q^T and
     // dP^T = V dO^T; L (log2 units) and Delta of the row
-    const E* Qh = Q + (int64_t)bh * M * D;
-    const E* dOh = dO + (int64_t)bh * M * D;
+    const E* Qh = Q + qr * D;
+    const E* dOh = dO + qr * D;
     V8 qf[T::kDS], of[T::kDS];
 #pragma unroll
     for (int s = 0; s < T::kDS; ++s) {
@@ -718,32 +811,49 @@ fa2_bwd_dq_kernel(const BwdParams p) {
             of[s] = V8{};
         }
     }
-    const float l2 = query < M ? p.lse[(int64_t)bh * M + query] * kLog2e : INFINITY;
-    const float dl = query < M ? p.delta[(int64_t)bh * M + query] : 0.f;
+    const float l2 = l2_of(query < M ? p.lse[qr + query] : INFINITY);
+    const float dl = query < M ? p.delta[qr + query] : 0.f;
 
-    const int kv_end = CAUSAL ? min(N, qt * T::kBM + T::kBM) : N;
-    const int n_kv = (kv_end + BN - 1) / BN;
-    int n_w = 0;  // K/V tiles this wave needs
-    if (qw0 < M) n_w = CAUSAL ? (min(N, qw0 + 32) + BN - 1) / BN : n_kv;
+    // K/V tiles [t0, t0 + n_kv): from the first key the workgroup's first row
+    // sees to the last key its last row sees; the wave needs [w0, w1) of them
+    int t0 = 0, n_kv = 0, w0 = 0, w1 = 0;
+    {
+        const int r0 = qt * T::kBM, r1 = min(r0 + T::kBM, M) - 1;
+        if (r0 <= r1) {
+            const int klo = key_lo<MASK>(p.wl, r0), khi = key_hi<MASK>(p.wr, r1, N);
+            if (klo <= khi) {
+                t0 = klo / BN;
+                n_kv = khi / BN + 1 - t0;
+            }
+        }
+        if (qw0 <= qw1) {
+            const int klo = key_lo<MASK>(p.wl, qw0), khi = key_hi<MASK>(p.wr, qw1, N);
+            if (klo <= khi) {
+                w0 = klo / BN - t0;
+                w1 = khi / BN + 1 - t0;
+            }
+        }
+    }
 
     floatx16 dqacc[T::kDB];
 #pragma unroll
     for (int db = 0; db < T::kDB; ++db) dqacc[db] = floatx16{};
 
-    const E* Kh = K + (int64_t)bkv * N * D;
-    const E* Vh = V + (int64_t)bkv * N * D;
+    const E* Kh = K + kvr * D;
+    const E* Vh = V + kvr * D;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     uint32_t cp_off[T::kLoadsPerWave];
     copy_offsets<D, T::kLoadsPerWave>(cp_off, wave, lane);
     TileReads<D> rd;
     rd.init(lane);
+    // kt: local tile, K/V tile t0 + kt of the sequence
     auto issue_tile = [&](int kt, char* kdst, char* vdst) {
-        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Kh, cp_off, wave_u, kt, N, kdst);
-        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Vh, cp_off, wave_u, kt, N, vdst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Kh, cp_off, wave_u, t0 + kt, N, kdst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Vh, cp_off, wave_u, t0 + kt, N, vdst);
     };
 
     auto compute_tile = [&](int kt, const char* ks, const char* vs) {
-        if (kt >= n_w) return;
+        if (kt < w0 || kt >= w1) return;
         // S^T = K Q^T, dP^T = V dO^T (rows: keys, columns: the wave's queries)
         floatx16 sacc[T::kKB], pacc[T::kKB];
 #pragma unroll
@@ -762,18 +872,22 @@ fa2_bwd_dq_kernel(const BwdParams p) {
                 pacc[kb] = Half<E>::mfma(va[kb], of[s], pacc[kb]);
             }
         }
-        // boundary tiles only: keys past N, (causal) keys after the query
-        const int kbase = kt * BN;
-        if (kbase + BN > N || (CAUSAL && kbase + BN - 1 > qw0)) {
+        // boundary tiles only: keys past N, or outside some row's causal or
+        // window range; key kbase + 32 kb + acc_row(r, h) is visible iff its
+        // compile-time part lies in [lim_lo, lim]
+        const int kbase = (t0 + kt) * BN;
+        if (kbase + BN > N || (MASK != kMaskNone && kbase + BN - 1 > key_hi<MASK>(p.wr, qw0, N)) ||
+            (MASK == kMaskLocal && kbase < key_lo<MASK>(p.wl, qw1))) {
             __asm__ volatile("");
-            int lim = N - 1 - kbase;
-            if (CAUSAL) lim = min(lim, query - kbase);
-            lim -= 4 * h;
+            const int lim = key_hi<MASK>(p.wr, query, N) - kbase - 4 * h;
+            const int lim_lo = key_lo<MASK>(p.wl, query) - kbase - 4 * h;
 #pragma unroll
             for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const int idx = 32 * kb + 8 * (r >> 2) + (r & 3);
+                    if (idx > lim || (MASK == kMaskLocal && idx < lim_lo)) sacc[kb][r] = -INFINITY;
+                }
         }
         // dS^T = P^T (dP^T - Delta), rounded once: B operand of dQ^T += K^T dS^T
         uint32_t sw[T::kKB][2][4];
@@ -817,7 +931,7 @@ fa2_bwd_dq_kernel(const BwdParams p) {
     // ---- epilogue: dQ = scale dS K, rounded to nearest even
     if (query < M) {
         const float scale = p.scale;
-        E* row = dQ + ((int64_t)bh * M + query) * D;
+        E* row = dQ + (qr + query) * D;
 #pragma unroll
         for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
@@ -834,7 +948,7 @@ fa2_bwd_dq_kernel(const BwdParams p) {
 // host side: validation, dispatch table, launches
 // ---------------------------------------------------------------------------
 struct BwdEntry {
-    int dtype, D, causal;
+    int dtype, D, mask;
     const void* delta;
     const void* dkdv;
     const void* dq;
@@ -849,71 +963,53 @@ struct BwdEntry {
 // kernel at this head dim).  D = 128: the wave-pair kernel (K and V in LDS, 8
 // waves per 128 keys), since K, V, dK and dV of 32 keys in VGPRs would leave
 // room for only one wave per SIMD.
-#define BWD_ROW64(E, code, causal)                                                                 \
-    {code, 64, causal, BWD_KERNEL(fa2_bwd_delta_kernel<E, 64>),                                  \
-     BWD_KERNEL(fa2_bwd_dkdv_kernel<E, 64, 64, 4, 2, causal>),                                   \
-     BWD_KERNEL(fa2_bwd_dq_kernel<E, 64, 64, 4, 2, causal>), 256, 128, 64, 256, 128, 64, 4 * 8}
-#define BWD_ROW128(E, code, causal)                                                                \
-    {code, 128, causal, BWD_KERNEL(fa2_bwd_delta_kernel<E, 128>),                                \
-     BWD_KERNEL(fa2_bwd_dkdv_pair_kernel<E, 128, causal>),                                       \
-     BWD_KERNEL(fa2_bwd_dq_kernel<E, 128, 32, 4, 2, causal>), 512, 128, 64, 256, 128, 32, 4 * 4}
+#define BWD_ROW64(E, code, mask)                                                                   \
+    {code, 64, mask, BWD_KERNEL(fa2_bwd_delta_kernel<E, 64>),                                    \
+     BWD_KERNEL(fa2_bwd_dkdv_kernel<E, 64, 64, 4, 2, mask>),                                     \
+     BWD_KERNEL(fa2_bwd_dq_kernel<E, 64, 64, 4, 2, mask>), 256, 128, 64, 256, 128, 64, 4 * 8}
+#define BWD_ROW128(E, code, mask)                                                                  \
+    {code, 128, mask, BWD_KERNEL(fa2_bwd_delta_kernel<E, 128>),                                  \
+     BWD_KERNEL(fa2_bwd_dkdv_pair_kernel<E, 128, mask>),                                         \
+     BWD_KERNEL(fa2_bwd_dq_kernel<E, 128, 32, 4, 2, mask>), 512, 128, 64, 256, 128, 32, 4 * 4}
+#define BWD_ROWS(E, code, mask) BWD_ROW64(E, code, mask), BWD_ROW128(E, code, mask)
 const BwdEntry kBwdTable[] = {
-    BWD_ROW64(__bf16, FA2_DTYPE_BF16, false),   BWD_ROW64(__bf16, FA2_DTYPE_BF16, true),
-    BWD_ROW128(__bf16, FA2_DTYPE_BF16, false),  BWD_ROW128(__bf16, FA2_DTYPE_BF16, true),
-    BWD_ROW64(_Float16, FA2_DTYPE_F16, false),  BWD_ROW64(_Float16, FA2_DTYPE_F16, true),
-    BWD_ROW128(_Float16, FA2_DTYPE_F16, false), BWD_ROW128(_Float16, FA2_DTYPE_F16, true),
+    BWD_ROWS(__bf16, FA2_DTYPE_BF16, kMaskNone),   BWD_ROWS(__bf16, FA2_DTYPE_BF16, kMaskCausal),
+    BWD_ROWS(__bf16, FA2_DTYPE_BF16, kMaskLocal),  BWD_ROWS(_Float16, FA2_DTYPE_F16, kMaskNone),
+    BWD_ROWS(_Float16, FA2_DTYPE_F16, kMaskCausal), BWD_ROWS(_Float16, FA2_DTYPE_F16, kMaskLocal),
 };
+#undef BWD_ROWS
 #undef BWD_ROW64
 #undef BWD_ROW128
 #undef BWD_KERNEL
 
-const BwdEntry* find_bwd_entry(int dtype, int64_t D, int causal) {
+const BwdEntry* find_bwd_entry(int dtype, int64_t D, int mask) {
     for (const BwdEntry& t : kBwdTable)
-        if (t.dtype == dtype && t.D == D && t.causal == causal) return &t;
+        if (t.dtype == dtype && t.D == D && t.mask == mask) return &t;
     return nullptr;
 }
 
-}  // namespace
-
-extern "C" int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                       const void* dout, void* dq, void* dk, void* dv, float* delta,
-                       int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
-                       float scale, int causal, int dtype, void* stream) {
-    // ---- argument checks, all before any HIP call
-    if (B < 0 || H < 0 || Hk < 1 || M < 0 || N <= 0 || D <= 0) return FA2_ERR_INVALID_ARGUMENT;
-    // a pointer may be null only when its buffer holds no element
-    const bool q_rows = B > 0 && H > 0 && M > 0, kv_rows = B > 0;
-    if (q_rows && (!q || !o || !lse || !dout || !dq || !delta)) return FA2_ERR_INVALID_ARGUMENT;
-    if (kv_rows && (!k || !v || !dk || !dv)) return FA2_ERR_INVALID_ARGUMENT;
-    if (H > 0 && (Hk > H || H % Hk != 0)) return FA2_ERR_INVALID_ARGUMENT;
+// Checks shared by every backward entry point: scale, flags, dtype, window
+// sides, alignment.  The rest (sizes, null pointers, overlaps) depends on the
+// layout.
+int bwd_common_checks(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, float* delta, int64_t H, int64_t Hk,
+                      float scale, int causal, int64_t wl, int64_t wr, int dtype) {
+    if (Hk < 1 || (H > 0 && (Hk > H || H % Hk != 0))) return FA2_ERR_INVALID_ARGUMENT;
     if (dtype != FA2_DTYPE_F32 && dtype != FA2_DTYPE_BF16 && dtype != FA2_DTYPE_F16) return FA2_ERR_INVALID_ARGUMENT;
     if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARGUMENT;
     if (!(scale > 0.f) || !isfinite(scale)) return FA2_ERR_INVALID_ARGUMENT;
+    if (wl < -1 || wr < -1) return FA2_ERR_INVALID_ARGUMENT;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
         misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) ||
         misaligned(lse, 4) || misaligned(delta, 4))
         return FA2_ERR_INVALID_ARGUMENT;
+    return FA2_OK;
+}
 
-    const BwdEntry* e = find_bwd_entry(dtype, D, causal);
-    if (!e) return FA2_ERR_UNSUPPORTED;
-
-    const int64_t kMax = (int64_t)1 << 31;
-    if (B > kMax || H > kMax || M >= kMax || N >= kMax) return FA2_ERR_UNSUPPORTED;
-    const int64_t BH = B * H, BHk = B * Hk;
-    if (M * D >= kMax || N * D >= kMax || BH * M >= kMax || BHk >= kMax) return FA2_ERR_UNSUPPORTED;
-    const KernelShape ks = kernel_shape(B, H, Hk, M, causal);
-    // one head's Q, dO (K, V) tiles are copied through a buffer resource whose
-    // byte size is a 32-bit int
-    if (ks.M * D * 2 >= kMax || N * D * 2 >= kMax) return FA2_ERR_UNSUPPORTED;
-    const int64_t n_kt = ceil_div(N, e->kv_block_n);
-    const int64_t n_qt_q = ceil_div(ks.M, e->q_block_m);
-    if (n_kt * BHk >= kMax || n_qt_q * ks.BH >= kMax) return FA2_ERR_UNSUPPORTED;
-
-    // the outputs (dq, dk, dv, delta) overlap no other buffer
-    const size_t elt = 2;
-    const size_t q_bytes = (size_t)BH * M * D * elt;
-    const size_t kv_bytes = (size_t)BHk * N * D * elt;
-    const size_t row_bytes = (size_t)BH * M * 4;
+// The outputs (dq, dk, dv, delta) overlap no other buffer.
+bool bwd_outputs_overlap(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta, size_t q_bytes,
+                         size_t kv_bytes, size_t row_bytes) {
     const struct {
         const void* p;
         size_t n;
@@ -922,41 +1018,155 @@ extern "C" int fa2_bwd(const void* q, const void* k, const void* v, const void* 
     constexpr int kOutputs = 4;
     for (int i = 0; i < kOutputs; ++i)
         for (int j = 0; j < (int)(sizeof(bufs) / sizeof(bufs[0])); ++j)
-            if (j != i && overlaps(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n)) return FA2_ERR_INVALID_ARGUMENT;
+            if (j != i && overlaps(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n)) return true;
+    return false;
+}
 
-    if (BHk == 0) return FA2_OK;  // no K/V rows: nothing to write
-
-    BwdParams prm;
-    prm.q = q; prm.k = k; prm.v = v; prm.dout = dout; prm.lse = lse; prm.delta = delta;
-    prm.dq = dq; prm.dk = dk; prm.dv = dv;
-    prm.BH = (int)ks.BH;
-    prm.BHk = (int)BHk;
-    prm.G = H > 0 ? (int)ks.G : 0;  // no query heads: dK = dV = 0
-    prm.M = (int)ks.M;
-    prm.N = (int)N;
-    prm.c_log2 = scale * kLog2e;
-    prm.scale = scale;
-
-    hipStream_t st = static_cast<hipStream_t>(stream);
+// The three launches: delta over `rows` rows, then dK/dV over n_kt key tiles
+// of every K/V head, then dQ over n_qt query tiles of every query head (the
+// kernel view's BH).
+int bwd_launch(const BwdEntry* e, BwdParams prm, int64_t rows, int64_t n_kt, int64_t n_qt_kv, int64_t n_qt,
+               const void* o, const void* dout, float* delta, hipStream_t st) {
     hipError_t err = hipSuccess;
-    const int rows = (int)(BH * M);
     if (rows > 0) {
         const void* o_arg = o;
         const void* do_arg = dout;
         float* d_arg = delta;
-        int r = rows;
+        int r = (int)rows;
         void* dargs[] = {(void*)&o_arg, (void*)&do_arg, &d_arg, &r};
         err = hipLaunchKernel(e->delta, dim3((unsigned)ceil_div(rows, e->delta_rows_per_wg)), dim3(256), dargs, 0, st);
     }
-    if (err == hipSuccess) {
-        prm.n_qt = (int)ceil_div(ks.M, e->kv_block_q);
+    if (err == hipSuccess && n_kt * prm.BHk > 0) {
+        prm.n_qt = (int)n_qt_kv;
         void* args[] = {&prm};
-        err = hipLaunchKernel(e->dkdv, dim3((unsigned)(n_kt * BHk)), dim3(e->kv_threads), args, 0, st);
+        err = hipLaunchKernel(e->dkdv, dim3((unsigned)(n_kt * prm.BHk)), dim3(e->kv_threads), args, 0, st);
     }
-    if (err == hipSuccess && rows > 0) {
-        prm.n_qt = (int)n_qt_q;
+    if (err == hipSuccess && rows > 0 && n_qt * prm.BH > 0) {
+        prm.n_qt = (int)n_qt;
         void* args[] = {&prm};
-        err = hipLaunchKernel(e->dq, dim3((unsigned)(n_qt_q * ks.BH)), dim3(e->q_threads), args, 0, st);
+        err = hipLaunchKernel(e->dq, dim3((unsigned)(n_qt * prm.BH)), dim3(e->q_threads), args, 0, st);
     }
     return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int fa2_bwd_local(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, float* delta,
+                             int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+                             float scale, int causal, int64_t window_left, int64_t window_right,
+                             int dtype, void* stream) {
+    // ---- argument checks, all before any HIP call
+    if (B < 0 || H < 0 || Hk < 1 || M < 0 || N <= 0 || D <= 0) return FA2_ERR_INVALID_ARGUMENT;
+    // a pointer may be null only when its buffer holds no element
+    const bool q_rows = B > 0 && H > 0 && M > 0, kv_rows = B > 0;
+    if (q_rows && (!q || !o || !lse || !dout || !dq || !delta)) return FA2_ERR_INVALID_ARGUMENT;
+    if (kv_rows && (!k || !v || !dk || !dv)) return FA2_ERR_INVALID_ARGUMENT;
+    const int chk = bwd_common_checks(q, k, v, o, lse, dout, dq, dk, dv, delta, H, Hk, scale, causal,
+                                      window_left, window_right, dtype);
+    if (chk != FA2_OK) return chk;
+
+    const int64_t kMax = (int64_t)1 << 31;
+    if (B > kMax || H > kMax || M >= kMax || N >= kMax) return FA2_ERR_UNSUPPORTED;
+    const int64_t BH = B * H, BHk = B * Hk;
+    if (M * D >= kMax || N * D >= kMax || BH * M >= kMax || BHk >= kMax) return FA2_ERR_UNSUPPORTED;
+    int64_t wl = window_left, wr = window_right;
+    const int mask = normalise_window(wl, wr, causal, M, N);
+    const BwdEntry* e = find_bwd_entry(dtype, D, mask);
+    if (!e) return FA2_ERR_UNSUPPORTED;
+    // without a mask the query heads of a K/V head form one row sequence
+    const KernelShape ks = kernel_shape(B, H, Hk, M, mask != kMaskNone);
+    // one head's Q, dO (K, V) tiles are copied through a buffer resource whose
+    // byte size is a 32-bit int
+    if (ks.M * D * 2 >= kMax || N * D * 2 >= kMax) return FA2_ERR_UNSUPPORTED;
+    const int64_t n_kt = ceil_div(N, e->kv_block_n);
+    const int64_t n_qt = ceil_div(ks.M, e->q_block_m);
+    if (n_kt * BHk >= kMax || n_qt * ks.BH >= kMax) return FA2_ERR_UNSUPPORTED;
+    const size_t q_bytes = (size_t)BH * M * D * 2, kv_bytes = (size_t)BHk * N * D * 2, row_bytes = (size_t)BH * M * 4;
+    if (bwd_outputs_overlap(q, k, v, o, lse, dout, dq, dk, dv, delta, q_bytes, kv_bytes, row_bytes))
+        return FA2_ERR_INVALID_ARGUMENT;
+
+    if (BHk == 0) return FA2_OK;  // no K/V rows: nothing to write
+
+    BwdParams prm{};  // dense layout: cu_q = cu_k = null
+    prm.q = q; prm.k = k; prm.v = v; prm.dout = dout; prm.lse = lse; prm.delta = delta;
+    prm.dq = dq; prm.dk = dk; prm.dv = dv;
+    prm.BH = (int)ks.BH;
+    prm.BHk = (int)BHk;
+    prm.H = (int)ks.H;
+    prm.Hk = (int)Hk;
+    prm.G = H > 0 ? (int)ks.G : 0;  // no query heads: dK = dV = 0
+    prm.M = (int)ks.M;
+    prm.N = (int)N;
+    prm.wl = (int)wl;
+    prm.wr = (int)wr;
+    prm.c_log2 = scale * kLog2e;
+    prm.scale = scale;
+    return bwd_launch(e, prm, BH * M, n_kt, ceil_div(ks.M, e->kv_block_q), n_qt, o, dout, delta,
+                      static_cast<hipStream_t>(stream));
+}
+
+extern "C" int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, float* delta,
+                       int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+                       float scale, int causal, int dtype, void* stream) {
+    return fa2_bwd_local(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hk, M, N, D, scale, causal, -1, -1,
+                         dtype, stream);
+}
+
+extern "C" int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, float* delta,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int64_t B, int64_t H, int64_t Hk, int64_t total_q, int64_t total_k,
+                              int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D, float scale, int causal,
+                              int64_t window_left, int64_t window_right, int dtype, void* stream) {
+    // ---- argument checks, all before any HIP call
+    if (B < 0 || H < 0 || Hk < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || D <= 0)
+        return FA2_ERR_INVALID_ARGUMENT;
+    if (max_seqlen_q > total_q || max_seqlen_k > total_k) return FA2_ERR_INVALID_ARGUMENT;
+    if (B > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return FA2_ERR_INVALID_ARGUMENT;
+    if (misaligned(cu_seqlens_q, 4) || misaligned(cu_seqlens_k, 4)) return FA2_ERR_INVALID_ARGUMENT;
+    if (H > 0 && total_q > 0 && (!q || !o || !lse || !dout || !dq || !delta)) return FA2_ERR_INVALID_ARGUMENT;
+    if (total_k > 0 && (!k || !v || !dk || !dv)) return FA2_ERR_INVALID_ARGUMENT;
+    const int chk = bwd_common_checks(q, k, v, o, lse, dout, dq, dk, dv, delta, H, Hk, scale, causal,
+                                      window_left, window_right, dtype);
+    if (chk != FA2_OK) return chk;
+
+    const int64_t kMax = (int64_t)1 << 31;
+    if (B >= kMax || H >= kMax || Hk >= kMax || total_q * D * 2 >= kMax || total_k * D * 2 >= kMax ||
+        H * total_q >= kMax)
+        return FA2_ERR_UNSUPPORTED;
+    int64_t wl = window_left, wr = window_right;
+    const int mask = normalise_window(wl, wr, causal, total_q, total_k);
+    const BwdEntry* e = find_bwd_entry(dtype, D, mask);
+    if (!e) return FA2_ERR_UNSUPPORTED;
+    const int64_t BH = B * H, BHk = B * Hk;
+    const int64_t n_kt = ceil_div(max_seqlen_k, e->kv_block_n);
+    const int64_t n_qt = ceil_div(max_seqlen_q, e->q_block_m);
+    if (BH >= kMax || n_kt * BHk >= kMax || n_qt * BH >= kMax) return FA2_ERR_UNSUPPORTED;
+    const size_t q_bytes = (size_t)H * total_q * D * 2, kv_bytes = (size_t)Hk * total_k * D * 2,
+                 row_bytes = (size_t)H * total_q * 4;
+    if (bwd_outputs_overlap(q, k, v, o, lse, dout, dq, dk, dv, delta, q_bytes, kv_bytes, row_bytes))
+        return FA2_ERR_INVALID_ARGUMENT;
+
+    if (BHk == 0) return FA2_OK;
+
+    BwdParams prm{};
+    prm.q = q; prm.k = k; prm.v = v; prm.dout = dout; prm.lse = lse; prm.delta = delta;
+    prm.dq = dq; prm.dk = dk; prm.dv = dv;
+    prm.cu_q = cu_seqlens_q;
+    prm.cu_k = cu_seqlens_k;
+    prm.total_q = (int)total_q;
+    prm.total_k = (int)total_k;
+    prm.BH = (int)BH;
+    prm.BHk = (int)BHk;
+    prm.H = (int)H;
+    prm.Hk = (int)Hk;
+    prm.G = H > 0 ? (int)(H / Hk) : 0;
+    prm.wl = (int)wl;
+    prm.wr = (int)wr;
+    prm.c_log2 = scale * kLog2e;
+    prm.scale = scale;
+    return bwd_launch(e, prm, H * total_q, n_kt, ceil_div(max_seqlen_q, e->kv_block_q), n_qt, o, dout, delta,
+                      static_cast<hipStream_t>(stream));
 }

@@ -121,6 +121,37 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Which keys a query row sees.
+constexpr int kMaskNone = 0;    // all of them
+constexpr int kMaskCausal = 1;  // key j visible to query i iff j <= i (top-left)
+constexpr int kMaskLocal = 2;   // sliding window i - wl <= j <= i + wr, either side unbounded when -1
+                                // (causal with a window is wr = 0)
+
+// First and last key that query row i of a sequence of N keys sees (lo > hi:
+// none), for window sides wl, wr.
+template <int MASK>
+__device__ __forceinline__ int key_lo(int wl, int i) {
+    return (MASK == kMaskLocal && wl >= 0) ? max(0, i - wl) : 0;
+}
+template <int MASK>
+__device__ __forceinline__ int key_hi(int wr, int i, int N) {
+    int hi = N - 1;
+    if (MASK == kMaskCausal) hi = min(hi, i);
+    if (MASK == kMaskLocal && wr >= 0) hi = min(hi, i + wr);
+    return hi;
+}
+// First and last query row of a sequence of M rows that sees key j (the
+// same relation read the other way).
+template <int MASK>
+__device__ __forceinline__ int query_lo(int wr, int j) {
+    if (MASK == kMaskCausal) return j;
+    return (MASK == kMaskLocal && wr >= 0) ? max(0, j - wr) : 0;
+}
+template <int MASK>
+__device__ __forceinline__ int query_hi(int wl, int j, int M) {
+    return (MASK == kMaskLocal && wl >= 0) ? min(M - 1, j + wl) : M - 1;
+}
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
@@ -150,6 +181,18 @@ KernelShape kernel_shape(int64_t B, int64_t H, int64_t Hk, int64_t M, int causal
     const int64_t G = H > 0 ? H / Hk : 1;
     if (!causal && G > 1) return {B * Hk, Hk, 1, M * G};
     return {B * H, H, G, M};
+}
+
+// Window sides as the kernels take them: causal is a right bound of 0; a
+// side that reaches past every row (left >= M, right >= N) is unbounded (-1),
+// which also keeps i - wl and i + wr inside int.  The mask kind follows.
+int normalise_window(int64_t& wl, int64_t& wr, int causal, int64_t M, int64_t N) {
+    if (causal) wr = 0;
+    if (wl >= M) wl = -1;
+    if (wr >= N) wr = -1;
+    if (wl < 0 && wr < 0) return kMaskNone;
+    if (wl < 0 && wr == 0) return kMaskCausal;
+    return kMaskLocal;
 }
 
 }  // namespace

@@ -88,23 +88,14 @@ struct FwdParams {
     float c_log2;         // scale * log2(e)
 };
 
-// Which keys a query row sees.
-constexpr int kMaskNone = 0;    // all of them
-constexpr int kMaskCausal = 1;  // key j visible to query i iff j <= i (top-left)
-constexpr int kMaskLocal = 2;   // sliding window i - wl <= j <= i + wr, either side unbounded when -1
-                                // (causal with a window is wr = 0)
-
 // First and last key query row i of a sequence of N keys sees (lo > hi: none).
 template <int MASK>
 __device__ __forceinline__ int key_lo(const FwdParams& p, int i) {
-    return (MASK == kMaskLocal && p.wl >= 0) ? max(0, i - p.wl) : 0;
+    return key_lo<MASK>(p.wl, i);
 }
 template <int MASK>
 __device__ __forceinline__ int key_hi(const FwdParams& p, int i, int N) {
-    int hi = N - 1;
-    if (MASK == kMaskCausal) hi = min(hi, i);
-    if (MASK == kMaskLocal && p.wr >= 0) hi = min(hi, i + p.wr);
-    return hi;
+    return key_hi<MASK>(p.wr, i, N);
 }
 
 // The (batch, head) sequence a workgroup works on: a head of the dense
@@ -1261,18 +1252,6 @@ const LocalEntry* find_local_entry(int dtype, int64_t D, int mask) {
     for (const LocalEntry& t : kLocalTable)
         if (t.dtype == dtype && t.D == D && t.mask == mask) return &t;
     return nullptr;
-}
-
-// Window sides as the kernels take them: causal is a right bound of 0; a
-// side that reaches past every row (left >= M, right >= N) is unbounded (-1),
-// which also keeps i - wl and i + wr inside int.  The mask kind follows.
-int normalise_window(int64_t& wl, int64_t& wr, int causal, int64_t M, int64_t N) {
-    if (causal) wr = 0;
-    if (wl >= M) wl = -1;
-    if (wr >= N) wr = -1;
-    if (wl < 0 && wr < 0) return kMaskNone;
-    if (wl < 0 && wr == 0) return kMaskCausal;
-    return kMaskLocal;
 }
 
 #undef FWD_KERNEL

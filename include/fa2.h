@@ -268,6 +268,38 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
             int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
             float scale, int causal, int dtype, void* stream);
 
+/*
+ * fa2_bwd_local -- fa2_bwd for the sliding-window forward (fa2_fwd_local):
+ * the same window_left / window_right rule decides which (query, key) pairs
+ * carry a gradient.  o and lse must come from fa2_fwd_local with the same
+ * window.  A row that saw no key (lse = -inf) gets dq = 0 and adds nothing
+ * to dk, dv.  Arguments, layout and errors as for fa2_bwd; window sides >= -1.
+ */
+int fa2_bwd_local(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, float* delta,
+                  int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+                  float scale, int causal, int64_t window_left, int64_t window_right,
+                  int dtype, void* stream);
+
+/*
+ * fa2_bwd_varlen -- fa2_bwd for packed variable-length sequences
+ * (fa2_fwd_varlen): q, o, dout, dq [H, total_q, D]; k, v, dk, dv
+ * [Hk, total_k, D]; lse, delta [H, total_q]; cu_seqlens_q / cu_seqlens_k
+ * int32 device offsets [B + 1] as for fa2_fwd_varlen.  max_seqlen_q and
+ * max_seqlen_k bound every sequence's query and key counts (they size the
+ * grids: rows or keys of a longer sequence past them are not computed);
+ * 0 <= max_seqlen_q <= total_q, 0 <= max_seqlen_k <= total_k.  Every key of
+ * a sequence gets dk, dv written (zero for keys no query sees).  Offsets are
+ * clamped on the device as in fa2_fwd_varlen.  Other arguments and errors as
+ * for fa2_bwd_local.
+ */
+int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, float* delta,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                   int64_t B, int64_t H, int64_t Hk, int64_t total_q, int64_t total_k,
+                   int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D, float scale, int causal,
+                   int64_t window_left, int64_t window_right, int dtype, void* stream);
+
 /* Static, NUL-terminated description of a fa2_status value. */
 const char* fa2_status_string(int status);
 

@@ -297,3 +297,45 @@ def test_varlen_unsupported_and_empty():
     assert call_varlen(B=0, cq=0, ck=0) == fa2.FA2_OK
     assert call_varlen(H=0) == fa2.FA2_OK
     assert call_varlen(max_q=0) == fa2.FA2_OK
+
+
+# ------------------------------------------- fa2_bwd_local / fa2_bwd_varlen (no launches)
+
+def call_bwd_local(wl=4, wr=4, **kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, delta=DL, B=1, H=2, Hk=2, M=16, N=16, D=64,
+                scale=0.125, causal=0, dtype=fa2.FA2_DTYPE_BF16)
+    args.update(kw)
+    a = args
+    return fa2.fa2_bwd_local(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["delta"],
+                             a["B"], a["H"], a["Hk"], a["M"], a["N"], a["D"], a["scale"], a["causal"], wl, wr,
+                             a["dtype"], None)
+
+
+def call_bwd_varlen(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, delta=DL, cq=CQ, ck=CK, B=2, H=2, Hk=2,
+             total_q=16, total_k=16, max_q=8, max_k=8, D=64, causal=0, wl=-1, wr=-1, dtype=fa2.FA2_DTYPE_BF16)
+    a.update(kw)
+    return fa2.fa2_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                              a["delta"], a["cq"], a["ck"], a["B"], a["H"], a["Hk"], a["total_q"], a["total_k"],
+                              a["max_q"], a["max_k"], a["D"], 0.125, a["causal"], a["wl"], a["wr"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(wl=-2), dict(wr=-3), dict(dq=0), dict(dk=Q), dict(N=0), dict(causal=3)])
+def test_bwd_local_bad_arguments_rejected(kw):
+    assert call_bwd_local(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_local_unsupported():
+    assert call_bwd_local(dtype=fa2.FA2_DTYPE_F32) == fa2.FA2_ERR_UNSUPPORTED
+    assert call_bwd_local(D=96) == fa2.FA2_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(cq=0), dict(ck=CK + 1), dict(max_q=17), dict(max_k=-1), dict(total_q=-1),
+                                dict(wl=-2), dict(dv=0), dict(delta=Q), dict(H=4, Hk=3)])
+def test_bwd_varlen_bad_arguments_rejected(kw):
+    assert call_bwd_varlen(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_varlen_unsupported_and_empty():
+    assert call_bwd_varlen(dtype=fa2.FA2_DTYPE_F32) == fa2.FA2_ERR_UNSUPPORTED
+    assert call_bwd_varlen(B=0, cq=0, ck=0) == fa2.FA2_OK

@@ -165,3 +165,70 @@ def test_backward_full_size_causal_4k_sampled_heads():
         sl = slice(b, b + 1), slice(h, h + 1)
         ref = oracle.attention_bwd(q[sl], k[sl], v[sl], do[sl], w.scale, w.causal)
         compare_grads([g[sl] for g in got], ref, w.dtype, f"full-size causal 4k slice b={b} h={h}")
+
+
+# --------------------------------------------- sliding window and packed sequences
+
+BWD_WINDOWS = [((16, 16), False), ((100, 0), False), ((70, -1), True), ((-1, 40), False), ((0, 0), False)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("M,N", [(300, 300), (200, 517), (700, 130)])
+@pytest.mark.parametrize("window,causal", BWD_WINDOWS)
+def test_backward_sliding_window(window, causal, M, N, D, dtype):
+    what = f"bwd local B=2 H=4 Hk=2 M={M} N={N} D={D} {dtype} causal={causal} window={window}"
+    note("case " + what)
+    q, k, v = workloads.make_inputs(2, 4, M, N, D, dtype, seed=M + N + D, Hk=2)
+    do = workloads.make_dout(2, 4, M, D, dtype, seed=M + N)
+    dev = [t.to("cuda") for t in (q, k, v, do)]
+    o, lse = fa2.forward(dev[0], dev[1], dev[2], causal=causal, window=window)
+    grads = fa2.backward(dev[0], dev[1], dev[2], o, lse, dev[3], causal=causal, window=window)
+    torch.cuda.synchronize()
+    got = tuple(t.float().cpu().numpy().astype(np.float64) for t in grads)
+    ref = oracle.attention_bwd(q, k, v, do, 1.0 / math.sqrt(D), causal, window=window)
+    compare_grads(got, ref, dtype, what)
+
+
+def test_autograd_function_with_window():
+    q, k, v = workloads.make_inputs(1, 2, 180, 180, 128, "bf16", 51)
+    do = workloads.make_dout(1, 2, 180, 128, "bf16", 51)
+    qd, kd, vd = (t.to("cuda").requires_grad_(True) for t in (q, k, v))
+    out = fa2.attention(qd, kd, vd, causal=True, window=(50, -1))
+    out.backward(do.to("cuda"))
+    torch.cuda.synchronize()
+    got = tuple(t.grad.float().cpu().numpy().astype(np.float64) for t in (qd, kd, vd))
+    ref = oracle.attention_bwd(q, k, v, do, 1.0 / math.sqrt(128), True, window=(50, -1))
+    compare_grads(got, ref, "bf16", "autograd with window (50, -1) causal")
+
+
+PACKED = [
+    ([1, 129, 0, 300, 64, 257], [1, 129, 0, 300, 64, 257]),
+    ([17, 250, 64, 1], [300, 3, 129, 700]),
+    ([40, 90, 7], [0, 120, 33]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("lens", PACKED, ids=["self", "cross", "nokeys"])
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (20, 3))])
+def test_backward_varlen(causal, window, lens, D, dtype):
+    lens_q, lens_k = lens
+    what = f"bwd varlen H=4 Hk=2 D={D} {dtype} causal={causal} window={window} lens_q={lens_q} lens_k={lens_k}"
+    note("case " + what)
+    cq = np.cumsum([0] + lens_q).astype(np.int32)
+    ck = np.cumsum([0] + lens_k).astype(np.int32)
+    q, _, _ = workloads.make_inputs(1, 4, int(cq[-1]), 1, D, dtype, seed=sum(lens_q) + D)
+    _, k, v = workloads.make_inputs(1, 2, 1, int(ck[-1]), D, dtype, seed=sum(lens_k) + D + 1)
+    do = workloads.make_dout(1, 4, int(cq[-1]), D, dtype, seed=sum(lens_q))
+    q, k, v, do = q[0].contiguous(), k[0].contiguous(), v[0].contiguous(), do[0].contiguous()
+    dev = [t.to("cuda") for t in (q, k, v, do)]
+    cqd, ckd = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    o, lse = fa2.forward_varlen(dev[0], dev[1], dev[2], cqd, ckd, max(lens_q), causal=causal, window=window)
+    grads = fa2.backward_varlen(dev[0], dev[1], dev[2], o, lse, dev[3], cqd, ckd, max(lens_q), max(lens_k),
+                                causal=causal, window=window)
+    torch.cuda.synchronize()
+    got = tuple(t.float().cpu().numpy().astype(np.float64) for t in grads)
+    ref = oracle.attention_bwd_varlen(q, k, v, do, cq, ck, 1.0 / math.sqrt(D), causal, window)
+    compare_grads(got, ref, dtype, what)
