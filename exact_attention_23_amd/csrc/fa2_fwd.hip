@@ -1118,33 +1118,56 @@ fa2_fwd_f32_kernel(const FwdParams p) {
 // partials combinable ("FlashAttention-2 from PyTorch to Triton", the role of
 // L; "From FlashAttention to FlashAttention 2", section "Layer 2", the
 // split-K/V path of the dispatch).
-// One wave per query row; each lane holds D / 64 consecutive values.
+// One wave per query row; each lane holds D / 64 consecutive values.  The
+// split logsumexps are loaded at once (lane i holds splits i and i + 64),
+// reduced across the wave, and the partial rows are then loaded eight splits
+// at a time, so a row costs a few memory latencies, not one per split.
 template <typename OutT, int D>
 __global__ void __launch_bounds__(256)
 fa2_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_l, OutT* __restrict__ O,
                  float* __restrict__ LSE, int rows, int n_splits) {
     constexpr int kPer = D / 64;
     static_assert(kPer == 1 || kPer == 2, "head dim");
+    static_assert(FA2_MAX_SPLITS <= 128, "two splits per lane");
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    float m = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) m = fmaxf(m, ws_l[(int64_t)s * rows + row]);
+    if (row >= rows) return;  // wave-uniform
+    const float la = lane < n_splits ? ws_l[(int64_t)lane * rows + row] : -INFINITY;
+    const float lb = lane + 64 < n_splits ? ws_l[(int64_t)(lane + 64) * rows + row] : -INFINITY;
+    float m = fmaxf(la, lb);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    // weights exp(L_s - m); a split that saw no visible key (L_s = -inf) has
+    // weight 0 and stored O_s = 0
+    const float wa = m == -INFINITY ? 0.f : fast_exp2((la - m) * kLog2e);
+    const float wb = m == -INFINITY ? 0.f : fast_exp2((lb - m) * kLog2e);
+    float wsum = wa + wb;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
     float acc[kPer] = {};
-    float wsum = 0.f;
-    if (m != -INFINITY) {
-        for (int s = 0; s < n_splits; ++s) {
-            const float w = fast_exp2((ws_l[(int64_t)s * rows + row] - m) * kLog2e);
-            if (w == 0.f) continue;  // a split that saw no visible key (L_s = -inf)
-            wsum += w;
-            const float* src = ws_o + ((int64_t)s * rows + row) * D + lane * kPer;
+    const float* base = ws_o + (int64_t)row * D + lane * kPer;
+    const int64_t split_stride = (int64_t)rows * D;
+    for (int s0 = 0; s0 < n_splits; s0 += 8) {
+        float x[8][kPer];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int s = min(s0 + j, n_splits - 1);  // past the last split: re-read it, weight 0
+            const float* src = base + s * split_stride;
             if constexpr (kPer == 2) {
-                const float2 x = *reinterpret_cast<const float2*>(src);
-                acc[0] = fmaf(w, x.x, acc[0]);
-                acc[1] = fmaf(w, x.y, acc[1]);
+                const float2 v = *reinterpret_cast<const float2*>(src);
+                x[j][0] = v.x;
+                x[j][1] = v.y;
             } else {
-                acc[0] = fmaf(w, src[0], acc[0]);
+                x[j][0] = src[0];
             }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int s = s0 + j;  // uniform across the wave
+            const float w_lane = s < 64 ? wa : wb;
+            const float w = s < n_splits ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_lane), s & 63)) : 0.f;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, x[j][i], acc[i]);
         }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -1187,6 +1210,23 @@ const Entry kTable[] = {
     {FA2_DTYPE_F32, 128, 0, FWD_PAIR(fa2_fwd_f32_kernel, 128, 32, 4, kMaskNone), 256, 128, 32, 1},
     {FA2_DTYPE_F32, 128, 1, FWD_PAIR(fa2_fwd_f32_kernel, 128, 32, 4, kMaskCausal), 256, 128, 32, 1},
 };
+// Few query rows per (K/V) head -- decoding, where M is one token or a few
+// per query head -- leave most of a 256-row workgroup empty, and the work is
+// reading K and V once.  These entries take 64 rows per workgroup (two
+// waves, one K/V tile double-buffered in 64 KiB of LDS, two workgroups per
+// CU), so that the split count that fills the GPU spreads the keys over more
+// workgroups and HBM, not the matrix core, sets the time.
+constexpr int64_t kShortRows = 64;  // rows per (K/V) head up to which kShortTable serves
+const Entry kShortTable[] = {
+    {FA2_DTYPE_BF16, 64, 0, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 64, 128, 2, 1, 2, kMaskNone), 128, 64, 128, 2},
+    {FA2_DTYPE_BF16, 64, 1, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 64, 128, 2, 1, 2, kMaskCausal), 128, 64, 128, 2},
+    {FA2_DTYPE_BF16, 128, 0, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 128, 64, 2, 1, 2, kMaskNone), 128, 64, 64, 2},
+    {FA2_DTYPE_BF16, 128, 1, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 128, 64, 2, 1, 2, kMaskCausal), 128, 64, 64, 2},
+    {FA2_DTYPE_F16, 64, 0, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 64, 128, 2, 1, 2, kMaskNone), 128, 64, 128, 2},
+    {FA2_DTYPE_F16, 64, 1, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 64, 128, 2, 1, 2, kMaskCausal), 128, 64, 128, 2},
+    {FA2_DTYPE_F16, 128, 0, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 128, 64, 2, 1, 2, kMaskNone), 128, 64, 64, 2},
+    {FA2_DTYPE_F16, 128, 1, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 128, 64, 2, 1, 2, kMaskCausal), 128, 64, 64, 2},
+};
 #undef FWD_PAIR
 
 struct MergeEntry {
@@ -1204,7 +1244,12 @@ const MergeEntry kMergeTable[] = {
 
 constexpr int kCUs = 256;  // MI355X; the split heuristic's design point
 
-const Entry* find_entry(int dtype, int64_t D, int causal) {
+// Kernel for (dtype, D, causal) at `rows` query rows per head of the kernel
+// view (the grouped rows of a K/V head when they are packed).
+const Entry* find_entry(int dtype, int64_t D, int causal, int64_t rows) {
+    if (rows <= kShortRows)
+        for (const Entry& t : kShortTable)
+            if (t.dtype == dtype && t.D == D && t.causal == causal) return &t;
     for (const Entry& t : kTable)
         if (t.dtype == dtype && t.D == D && t.causal == causal) return &t;
     return nullptr;
@@ -1275,9 +1320,9 @@ extern "C" int fa2_fwd_num_splits(int64_t B, int64_t H, int64_t Hk, int64_t M, i
     if (B < 0 || H < 0 || Hk < 1 || M < 0 || N <= 0) return 1;
     if (H > 0 && (Hk > H || H % Hk != 0)) return 1;
     if (B > ((int64_t)1 << 31) || H > ((int64_t)1 << 31) || M > ((int64_t)1 << 31)) return 1;
-    const Entry* e = find_entry(dtype, D, causal);
-    if (!e) return 1;
     const KernelShape ks = kernel_shape(B, H, Hk, M, causal);
+    const Entry* e = find_entry(dtype, D, causal, ks.M);
+    if (!e) return 1;
     return choose_splits(*e, ks.BH, ks.M, N);
 }
 
@@ -1300,8 +1345,7 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
         misaligned(lse, 4))
         return FA2_ERR_INVALID_ARGUMENT;
 
-    const Entry* e = find_entry(dtype, D, causal);
-    if (!e) return FA2_ERR_UNSUPPORTED;
+    if (!find_entry(dtype, D, causal, kShortRows + 1)) return FA2_ERR_UNSUPPORTED;
 
     // sizes: per-head offsets are 32-bit in the kernels, the grid is 1-D
     const int64_t kMax = (int64_t)1 << 31;
@@ -1310,6 +1354,7 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
     if (M * D >= kMax || N * D >= kMax || BH >= kMax) return FA2_ERR_UNSUPPORTED;
     const KernelShape ks = kernel_shape(B, H, Hk, M, causal);
     if (ks.M * D >= kMax) return FA2_ERR_UNSUPPORTED;
+    const Entry* e = find_entry(dtype, D, causal, ks.M);
     // the 16-bit kernels address one head's K (V) through a buffer resource
     // whose byte size is a 32-bit int
     if (dtype != FA2_DTYPE_F32 && N * D * 2 >= kMax) return FA2_ERR_UNSUPPORTED;

@@ -84,6 +84,23 @@ def test_split_kv_decode_shapes_auto(M, dtype):
     check(B, H, 2, M, N, D, dtype, False, n_splits=0, seed=M)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("M,N,H,Hk,n_splits", [
+    (1, 3000, 8, 1, 0),      # one token per query head, 8 heads on one K/V head
+    (16, 777, 8, 2, 1),      # 64 grouped rows, unsplit, ragged N
+    (8, 5000, 32, 4, 0),     # 64 grouped rows, automatic splits
+    (33, 129, 4, 4, 3),      # explicit splits over a short key range
+    (64, 1000, 2, 2, 0),     # the largest row count of the few-row kernels
+    (65, 1000, 2, 2, 0),     # one row more: the 256-row kernels
+])
+def test_few_query_rows(M, N, H, Hk, n_splits, causal, D, dtype):
+    # rows per (K/V) head <= 64 run the 64-row workgroups; the result must not
+    # depend on which kernel served it beyond the tolerances
+    check(2, H, Hk, M, N, D, dtype, causal, n_splits=n_splits, seed=M * 7 + N)
+
+
 def test_split_kv_large_magnitude():
     # scores far beyond fp32 exp range in every split (the workload with
     # qk_sigma = 4): the merge must rescale by logsumexp differences only
