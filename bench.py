@@ -19,7 +19,8 @@ non-causal).  Prints ONE JSON line with the whole-job throughput
 * workloads: per-launch latency (median of 100 after 25 warm-ups, with and
   without an L2/MALL flush before each launch) of every workload;
 * backward: per-call latency of fa2_bwd (delta, dK/dV and dQ kernels) on the
-  16-bit workloads, counted as 10*B*H*M*N*D flop (halved for causal).
+  workloads of workloads.BACKWARD, counted as 10*B*H*M*N*D flop (halved for
+  causal).
 
 With --pass bwd the timed step is one fa2_bwd call instead (the forward's o
 and lse are computed once beforehand), counted the same way.
@@ -85,11 +86,14 @@ def load_traffic(workload: str):
 def dominant_kernel(w, splits: int = 1) -> str:
     """The forward kernel the library launches for this workload (its
     dispatch table: fp32 kernel, or the 16-bit kernel, ping-pong at D=128
-    on the dense unwindowed path), followed by the combine kernel when the
-    key range is split."""
+    on the dense unwindowed path unless a head has at most 64 rows),
+    followed by the combine kernel when the key range is split."""
+    # rows per head of the kernel view: the grouped query heads of a K/V head
+    # form one row sequence when there is no mask
+    rows = w.M * (w.H // w.kv_heads) if not w.causal and w.window == (-1, -1) else w.M
     if w.dtype == "f32":
         k = "fa2_fwd_f32_kernel"
-    elif w.lengths is not None or w.window != (-1, -1):
+    elif w.lengths is not None or w.window != (-1, -1) or rows <= 64:
         k = "fa2_fwd_half_kernel"
     else:
         k = "fa2_fwd_half_pp_kernel" if w.D == 128 else "fa2_fwd_half_kernel"
@@ -235,7 +239,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="mha_f32_2k")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
-                    help="time the forward (default) or the backward pass (fa2_bwd, 16-bit workloads)")
+                    help="time the forward (default) or the backward pass (fa2_bwd)")
     ap.add_argument("--prewarm", type=float, default=0.3,
                     help="seconds of back-to-back untimed steps before the warm-up steps (clock settling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -342,10 +346,6 @@ def main(argv=None):
 
     w = workloads.get(args.workload)
     backward = args.which == "bwd"
-    if backward and w.dtype == "f32":
-        print(json.dumps({"error": "the backward pass has 16-bit kernels only; pick a bf16/f16 workload"}),
-              flush=True)
-        return 2
     if backward:
         bufs = bwd_setup(w)
         fn = bwd_launcher(w, bufs)

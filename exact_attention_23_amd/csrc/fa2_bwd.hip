@@ -945,6 +945,414 @@ fa2_bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// fp32 backward (v_mfma_f32_32x32x2_f32: true fp32 products, P and dS kept in
+// fp32 as MFMA operands)
+// ---------------------------------------------------------------------------
+// MFMA step s of a product over d contracts d = h D/2 + s in lane half h of
+// both operands (as in the fp32 forward), so a lane reads four consecutive
+// d of a row at once; step r of a product over the rows of a 32-row block
+// contracts rows acc_row(r, 0) and acc_row(r, 1), the rows whose P (or dS)
+// the lane's accumulator register r holds.  Tiles live in LDS as fp32 rows
+// padded to D + 4 floats: 16 consecutive rows read at one d then start 4
+// banks apart.
+
+// Delta = rowsum(dO o O): D / 4 lanes per row, 16 bytes each.
+template <int D>
+__global__ void __launch_bounds__(256)
+fa2_bwd_delta_f32_kernel(const float* __restrict__ O, const float* __restrict__ dO, float* __restrict__ delta,
+                         int rows) {
+    constexpr int kLanes = D / 4;
+    constexpr int kRowsPerWave = 64 / kLanes;
+    const int lane = threadIdx.x & 63;
+    const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave + lane / kLanes;
+    const int c = lane % kLanes;
+    float acc = 0.f;
+    if (row < rows) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(O + (int64_t)row * D + 4 * c);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(dO + (int64_t)row * D + 4 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(a[i], b[i], acc);
+    }
+#pragma unroll
+    for (int off = kLanes / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && c == 0) delta[row] = acc;
+}
+
+template <int D>
+struct BwdF32Traits {
+    static constexpr int kNW = 4;
+    static constexpr int kThreads = kNW * 64;
+    static constexpr int kRows = 32;                  // rows per streamed tile (queries or keys)
+    static constexpr int kBlock = 32 * kNW;           // keys (dK/dV) or queries (dQ) per workgroup
+    static constexpr int kDB = D / 32;
+    static constexpr int kHalfD = D / 2;
+    static constexpr int kStr = D + 4;                // floats per LDS row
+    static constexpr int kTileElems = kRows * kStr;
+    static constexpr int kChunks = kRows * D / 4;     // 16-byte chunks per tile
+    static constexpr int kPerThread = kChunks / kThreads;
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(kChunks % kThreads == 0, "loader split");
+};
+
+// Rows [row0, row0 + 32) of a head's [rows, D] fp32 matrix through registers
+// into an LDS tile; rows at or past `n` are zero.
+template <int D>
+struct F32TileLoader {
+    using T = BwdF32Traits<D>;
+    u32x4 a[T::kPerThread], b[T::kPerThread];
+    __device__ __forceinline__ void load(const float* A, const float* B, int row0, int n, int tid) {
+#pragma unroll
+        for (int i = 0; i < T::kPerThread; ++i) {
+            const int id = tid + i * T::kThreads;
+            const int r = row0 + id / (D / 4), c4 = id % (D / 4);
+            const bool ok = r < n;
+            a[i] = ok ? *reinterpret_cast<const u32x4*>(A + (int64_t)r * D + 4 * c4) : u32x4{0, 0, 0, 0};
+            b[i] = ok ? *reinterpret_cast<const u32x4*>(B + (int64_t)r * D + 4 * c4) : u32x4{0, 0, 0, 0};
+        }
+    }
+    __device__ __forceinline__ void store(float* sa, float* sb, int tid) const {
+#pragma unroll
+        for (int i = 0; i < T::kPerThread; ++i) {
+            const int id = tid + i * T::kThreads;
+            const int r = id / (D / 4), c4 = id % (D / 4);
+            *reinterpret_cast<u32x4*>(sa + r * T::kStr + 4 * c4) = a[i];
+            *reinterpret_cast<u32x4*>(sb + r * T::kStr + 4 * c4) = b[i];
+        }
+    }
+};
+
+// dK, dV: one workgroup of 4 waves per (128-key tile, K/V head); each wave
+// owns 32 keys and keeps their K and V rows in registers; Q and dO stream
+// through LDS 32 rows at a time.
+template <int D, int MASK>
+__global__ void __launch_bounds__(256, 1)
+fa2_bwd_dkdv_f32_kernel(const BwdParams p) {
+    using T = BwdF32Traits<D>;
+    const float* __restrict__ Q = static_cast<const float*>(p.q);
+    const float* __restrict__ K = static_cast<const float*>(p.k);
+    const float* __restrict__ V = static_cast<const float*>(p.v);
+    const float* __restrict__ dO = static_cast<const float*>(p.dout);
+    float* __restrict__ dK = static_cast<float*>(p.dk);
+    float* __restrict__ dV = static_cast<float*>(p.dv);
+    const float c_log2 = p.c_log2;
+    __shared__ __attribute__((aligned(16))) float sQ[2][T::kTileElems];
+    __shared__ __attribute__((aligned(16))) float sO[2][T::kTileElems];
+    __shared__ __attribute__((aligned(16))) float sL[2][T::kRows], sD[2][T::kRows];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+
+    // key tiles major (under a causal mask the first key tile has the most
+    // query tiles), K/V heads fastest
+    const int bkv = blockIdx.x % p.BHk;
+    const int kt = blockIdx.x / p.BHk;
+    const BwdSeq sq = bwd_seq(p, p.cu_q ? bkv / p.Hk : 0);
+    const int M = sq.M, N = sq.N;
+    const int64_t kvr = kv_row0(p, sq, bkv);
+    const int kbase = kt * T::kBlock;
+    const int k0 = kbase + 32 * wave;  // first key of this wave
+    const int key = k0 + l32;          // this lane's key
+
+    // K and V rows of the lane's key, d half h: B operands of S = Q K^T and
+    // dP = dO V^T
+    float kf[T::kHalfD], vf[T::kHalfD];
+#pragma unroll
+    for (int s = 0; s < T::kHalfD; s += 4) {
+        floatx4 x = floatx4{0.f, 0.f, 0.f, 0.f}, y = x;
+        if (key < N) {
+            x = *reinterpret_cast<const floatx4*>(K + (kvr + key) * D + h * T::kHalfD + s);
+            y = *reinterpret_cast<const floatx4*>(V + (kvr + key) * D + h * T::kHalfD + s);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            kf[s + u] = x[u];
+            vf[s + u] = y[u];
+        }
+    }
+
+    // query tiles: every query head of the group, the 32-row tiles whose rows
+    // see some key of the workgroup
+    int qt0, qt1;
+    query_tiles<MASK>(p, kbase, min(kbase + T::kBlock, N) - 1, M, T::kRows, qt0, qt1);
+    const int per_g = qt1 - qt0;
+    const int n_it = p.G * per_g;
+
+    floatx16 dkacc[T::kDB], dvacc[T::kDB];
+#pragma unroll
+    for (int db = 0; db < T::kDB; ++db) dkacc[db] = dvacc[db] = floatx16{};
+
+    auto tile_head = [&](int it, int& bh, int& qt) {
+        const int g = it / per_g;
+        qt = qt0 + (it - g * per_g);
+        bh = bkv * p.G + g;
+    };
+    F32TileLoader<D> ld;
+    float ld_next = 0.f;  // the next tile's L (log2 units, wave 0) or Delta (wave 1) of row `lane`
+    auto fetch = [&](int it) {
+        int bh, qt;
+        tile_head(it, bh, qt);
+        const int64_t qr = q_row0(p, sq, bh);
+        ld.load(Q + qr * D, dO + qr * D, qt * T::kRows, M, tid);
+        const int row = qt * T::kRows + lane;
+        if (wave == 0) ld_next = l2_of(row < M ? p.lse[qr + row] : INFINITY);
+        else if (wave == 1) ld_next = row < M ? p.delta[qr + row] : 0.f;
+    };
+    auto stash = [&](int buf) {
+        ld.store(sQ[buf], sO[buf], tid);
+        if (lane < T::kRows) {
+            if (wave == 0) sL[buf][lane] = ld_next;
+            else if (wave == 1) sD[buf][lane] = ld_next;
+        }
+    };
+
+    auto compute_tile = [&](int it, int buf) {
+        int bh, qt;
+        tile_head(it, bh, qt);
+        const int r0 = qt * T::kRows;
+        if (!block_live<MASK>(p, r0, k0, M, N)) return;
+        const float* qs = sQ[buf];
+        const float* os = sO[buf];
+        // S = Q K^T and dP = dO V^T (rows: the tile's queries, columns: the
+        // wave's keys)
+        floatx16 sacc = floatx16{}, pacc = floatx16{};
+        const float* qrow = qs + l32 * T::kStr + h * T::kHalfD;
+        const float* orow = os + l32 * T::kStr + h * T::kHalfD;
+#pragma unroll
+        for (int s = 0; s < T::kHalfD; s += 4) {
+            const floatx4 qa = *reinterpret_cast<const floatx4*>(qrow + s);
+            const floatx4 oa = *reinterpret_cast<const floatx4*>(orow + s);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[u], kf[s + u], sacc, 0, 0, 0);
+                pacc = __builtin_amdgcn_mfma_f32_32x32x2f32(oa[u], vf[s + u], pacc, 0, 0, 0);
+            }
+        }
+        if (MASK != kMaskNone && !block_full<MASK>(p, r0, k0)) {
+            __asm__ volatile("");  // keep this a branch, not a select per element
+            mask_rows<MASK>(p, sacc, r0, h, key);
+        }
+        // P = exp2(S c - L2), dS = P (dP - Delta); register r holds query
+        // r0 + acc_row(r, h)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const floatx4 l4 = *reinterpret_cast<const floatx4*>(&sL[buf][8 * g + 4 * h]);
+            const floatx4 d4 = *reinterpret_cast<const floatx4*>(&sD[buf][8 * g + 4 * h]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float pv = fast_exp2(fmaf(sacc[4 * g + u], c_log2, -l4[u]));
+                sacc[4 * g + u] = pv;
+                pacc[4 * g + u] = pv * (pacc[4 * g + u] - d4[u]);
+            }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS: step r contracts the rows whose
+        // P and dS the lane's register r holds
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = acc_row(r, h);
+#pragma unroll
+            for (int db = 0; db < T::kDB; ++db) {
+                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(os[row * T::kStr + 32 * db + l32], sacc[r], dvacc[db], 0, 0, 0);
+                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[row * T::kStr + 32 * db + l32], pacc[r], dkacc[db], 0, 0, 0);
+            }
+        }
+    };
+
+    if (n_it > 0) {
+        fetch(0);
+        stash(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < n_it; ++it) {
+        const int buf = it & 1;
+        const bool has_next = it + 1 < n_it;
+        if (has_next) fetch(it + 1);
+        compute_tile(it, buf);
+        if (has_next) stash(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: dK = scale dS^T Q, dV = P^T dO; register r of block db
+    // holds d = 32 db + acc_row(r, h) of the lane's key
+    if (key < N) {
+        const float scale = p.scale;
+        float* krow = dK + (kvr + key) * D;
+        float* vrow = dV + (kvr + key) * D;
+#pragma unroll
+        for (int db = 0; db < T::kDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * db + 8 * g + 4 * h;
+                *reinterpret_cast<floatx4*>(krow + d) =
+                    floatx4{dkacc[db][4 * g] * scale, dkacc[db][4 * g + 1] * scale, dkacc[db][4 * g + 2] * scale,
+                            dkacc[db][4 * g + 3] * scale};
+                *reinterpret_cast<floatx4*>(vrow + d) =
+                    floatx4{dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]};
+            }
+    }
+}
+
+// dQ: one workgroup of 4 waves per (128-query tile, query head); each wave
+// owns 32 queries and keeps their Q and dO rows in registers; K and V stream
+// through LDS 32 keys at a time.
+template <int D, int MASK>
+__global__ void __launch_bounds__(256, 1)
+fa2_bwd_dq_f32_kernel(const BwdParams p) {
+    using T = BwdF32Traits<D>;
+    const float* __restrict__ Q = static_cast<const float*>(p.q);
+    const float* __restrict__ K = static_cast<const float*>(p.k);
+    const float* __restrict__ V = static_cast<const float*>(p.v);
+    const float* __restrict__ dO = static_cast<const float*>(p.dout);
+    float* __restrict__ dQ = static_cast<float*>(p.dq);
+    const float c_log2 = p.c_log2;
+    __shared__ __attribute__((aligned(16))) float sK[2][T::kTileElems];
+    __shared__ __attribute__((aligned(16))) float sV[2][T::kTileElems];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+
+    // query tiles major (heaviest first under a causal mask), heads fastest
+    const int bh = blockIdx.x % p.BH;
+    int qt = blockIdx.x / p.BH;
+    if (MASK == kMaskCausal) qt = p.n_qt - 1 - qt;
+    const int bkv = p.G == 1 ? bh : bh / p.G;
+    const BwdSeq sq = bwd_seq(p, p.cu_q ? bh / p.H : 0);
+    const int M = sq.M, N = sq.N;
+    const int64_t qr = q_row0(p, sq, bh), kvr = kv_row0(p, sq, bkv);
+    const int qw0 = qt * T::kBlock + 32 * wave;  // first query row of this wave
+    const int qw1 = min(qw0 + 32, M) - 1;        // its last row
+    const int query = qw0 + l32;                 // this lane's query row
+
+    // Q and dO rows of the lane's query, d half h: B operands of S^T = K Q^T
+    // and dP^T = V dO^T; L (log2 units) and Delta of the row
+    float qf[T::kHalfD], of[T::kHalfD];
+#pragma unroll
+    for (int s = 0; s < T::kHalfD; s += 4) {
+        floatx4 x = floatx4{0.f, 0.f, 0.f, 0.f}, y = x;
+        if (query < M) {
+            x = *reinterpret_cast<const floatx4*>(Q + (qr + query) * D + h * T::kHalfD + s);
+            y = *reinterpret_cast<const floatx4*>(dO + (qr + query) * D + h * T::kHalfD + s);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            qf[s + u] = x[u];
+            of[s + u] = y[u];
+        }
+    }
+    const float l2 = l2_of(query < M ? p.lse[qr + query] : INFINITY);
+    const float dl = query < M ? p.delta[qr + query] : 0.f;
+
+    // 32-key tiles [t0, t0 + n_kv): from the first key the workgroup's first
+    // row sees to the last key its last row sees; the wave needs [w0, w1)
+    constexpr int BN = T::kRows;
+    int t0 = 0, n_kv = 0, w0 = 0, w1 = 0;
+    {
+        const int r0 = qt * T::kBlock, r1 = min(r0 + T::kBlock, M) - 1;
+        if (r0 <= r1) {
+            const int klo = key_lo<MASK>(p.wl, r0), khi = key_hi<MASK>(p.wr, r1, N);
+            if (klo <= khi) {
+                t0 = klo / BN;
+                n_kv = khi / BN + 1 - t0;
+            }
+        }
+        if (qw0 <= qw1) {
+            const int klo = key_lo<MASK>(p.wl, qw0), khi = key_hi<MASK>(p.wr, qw1, N);
+            if (klo <= khi) {
+                w0 = klo / BN - t0;
+                w1 = khi / BN + 1 - t0;
+            }
+        }
+    }
+    const int lim_hi = key_hi<MASK>(p.wr, query, N), lim_lo = key_lo<MASK>(p.wl, query);
+
+    floatx16 dqacc[T::kDB];
+#pragma unroll
+    for (int db = 0; db < T::kDB; ++db) dqacc[db] = floatx16{};
+
+    F32TileLoader<D> ld;
+    const float* Kh = K + kvr * D;
+    const float* Vh = V + kvr * D;
+
+    auto compute_tile = [&](int kt, int buf) {
+        if (kt < w0 || kt >= w1) return;
+        const float* ks = sK[buf];
+        const float* vs = sV[buf];
+        // S^T = K Q^T, dP^T = V dO^T (rows: the tile's keys, columns: the
+        // wave's queries)
+        floatx16 sacc = floatx16{}, pacc = floatx16{};
+        const float* krow = ks + l32 * T::kStr + h * T::kHalfD;
+        const float* vrow = vs + l32 * T::kStr + h * T::kHalfD;
+#pragma unroll
+        for (int s = 0; s < T::kHalfD; s += 4) {
+            const floatx4 ka = *reinterpret_cast<const floatx4*>(krow + s);
+            const floatx4 va = *reinterpret_cast<const floatx4*>(vrow + s);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[u], qf[s + u], sacc, 0, 0, 0);
+                pacc = __builtin_amdgcn_mfma_f32_32x32x2f32(va[u], of[s + u], pacc, 0, 0, 0);
+            }
+        }
+        // keys outside the lane's visible range (past N, causal, window):
+        // register r holds key kbase + acc_row(r, h)
+        const int kbase = (t0 + kt) * BN;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kk = kbase + acc_row(r, h);
+            if (kk > lim_hi || kk < lim_lo) sacc[r] = -INFINITY;
+        }
+        // dS^T = P^T (dP^T - Delta), then dQ^T += K^T dS^T: step r contracts
+        // the keys whose dS the lane's register r holds
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pv = fast_exp2(fmaf(sacc[r], c_log2, -l2));
+            pacc[r] = pv * (pacc[r] - dl);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = acc_row(r, h);
+#pragma unroll
+            for (int db = 0; db < T::kDB; ++db)
+                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[row * T::kStr + 32 * db + l32], pacc[r], dqacc[db], 0, 0, 0);
+        }
+    };
+
+    if (n_kv > 0) {
+        ld.load(Kh, Vh, t0 * BN, N, tid);
+        ld.store(sK[0], sV[0], tid);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < n_kv; ++kt) {
+        const int buf = kt & 1;
+        const bool has_next = kt + 1 < n_kv;
+        if (has_next) ld.load(Kh, Vh, (t0 + kt + 1) * BN, N, tid);
+        compute_tile(kt, buf);
+        if (has_next) ld.store(sK[buf ^ 1], sV[buf ^ 1], tid);
+        __syncthreads();
+    }
+
+    // ---- epilogue: dQ = scale dS K; register r of block db holds
+    // d = 32 db + acc_row(r, h) of the lane's query
+    if (query < M) {
+        const float scale = p.scale;
+        float* row = dQ + (qr + query) * D;
+#pragma unroll
+        for (int db = 0; db < T::kDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * db + 8 * g + 4 * h;
+                *reinterpret_cast<floatx4*>(row + d) =
+                    floatx4{dqacc[db][4 * g] * scale, dqacc[db][4 * g + 1] * scale, dqacc[db][4 * g + 2] * scale,
+                            dqacc[db][4 * g + 3] * scale};
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side: validation, dispatch table, launches
 // ---------------------------------------------------------------------------
 struct BwdEntry {
@@ -972,11 +1380,21 @@ struct BwdEntry {
      BWD_KERNEL(fa2_bwd_dkdv_pair_kernel<E, 128, mask>),                                         \
      BWD_KERNEL(fa2_bwd_dq_kernel<E, 128, 32, 4, 2, mask>), 512, 128, 64, 256, 128, 32, 4 * 4}
 #define BWD_ROWS(E, code, mask) BWD_ROW64(E, code, mask), BWD_ROW128(E, code, mask)
+// fp32: 4 waves x 32 keys (dK/dV) or 32 queries (dQ) per workgroup, 32-row
+// streamed tiles; the delta kernel covers 64 / (D / 4) rows per wave
+#define BWD_ROW_F32(D, mask)                                                                       \
+    {FA2_DTYPE_F32, D, mask, BWD_KERNEL(fa2_bwd_delta_f32_kernel<D>),                             \
+     BWD_KERNEL(fa2_bwd_dkdv_f32_kernel<D, mask>), BWD_KERNEL(fa2_bwd_dq_f32_kernel<D, mask>),     \
+     256, 128, 32, 256, 128, 32, 4 * (256 / D)}
+#define BWD_ROWS_F32(mask) BWD_ROW_F32(64, mask), BWD_ROW_F32(128, mask)
 const BwdEntry kBwdTable[] = {
     BWD_ROWS(__bf16, FA2_DTYPE_BF16, kMaskNone),   BWD_ROWS(__bf16, FA2_DTYPE_BF16, kMaskCausal),
     BWD_ROWS(__bf16, FA2_DTYPE_BF16, kMaskLocal),  BWD_ROWS(_Float16, FA2_DTYPE_F16, kMaskNone),
     BWD_ROWS(_Float16, FA2_DTYPE_F16, kMaskCausal), BWD_ROWS(_Float16, FA2_DTYPE_F16, kMaskLocal),
+    BWD_ROWS_F32(kMaskNone), BWD_ROWS_F32(kMaskCausal), BWD_ROWS_F32(kMaskLocal),
 };
+#undef BWD_ROWS_F32
+#undef BWD_ROW_F32
 #undef BWD_ROWS
 #undef BWD_ROW64
 #undef BWD_ROW128
@@ -1076,13 +1494,15 @@ extern "C" int fa2_bwd_local(const void* q, const void* k, const void* v, const 
     if (!e) return FA2_ERR_UNSUPPORTED;
     // without a mask the query heads of a K/V head form one row sequence
     const KernelShape ks = kernel_shape(B, H, Hk, M, mask != kMaskNone);
-    // one head's Q, dO (K, V) tiles are copied through a buffer resource whose
-    // byte size is a 32-bit int
-    if (ks.M * D * 2 >= kMax || N * D * 2 >= kMax) return FA2_ERR_UNSUPPORTED;
+    // the 16-bit kernels copy one head's Q, dO (K, V) tiles through a buffer
+    // resource whose byte size is a 32-bit int
+    if (dtype != FA2_DTYPE_F32 && (ks.M * D * 2 >= kMax || N * D * 2 >= kMax)) return FA2_ERR_UNSUPPORTED;
     const int64_t n_kt = ceil_div(N, e->kv_block_n);
     const int64_t n_qt = ceil_div(ks.M, e->q_block_m);
     if (n_kt * BHk >= kMax || n_qt * ks.BH >= kMax) return FA2_ERR_UNSUPPORTED;
-    const size_t q_bytes = (size_t)BH * M * D * 2, kv_bytes = (size_t)BHk * N * D * 2, row_bytes = (size_t)BH * M * 4;
+    const size_t elt = dtype == FA2_DTYPE_F32 ? 4 : 2;
+    const size_t q_bytes = (size_t)BH * M * D * elt, kv_bytes = (size_t)BHk * N * D * elt,
+                 row_bytes = (size_t)BH * M * 4;
     if (bwd_outputs_overlap(q, k, v, o, lse, dout, dq, dk, dv, delta, q_bytes, kv_bytes, row_bytes))
         return FA2_ERR_INVALID_ARGUMENT;
 
@@ -1133,7 +1553,9 @@ extern "C" int fa2_bwd_varlen(const void* q, const void* k, const void* v, const
     if (chk != FA2_OK) return chk;
 
     const int64_t kMax = (int64_t)1 << 31;
-    if (B >= kMax || H >= kMax || Hk >= kMax || total_q * D * 2 >= kMax || total_k * D * 2 >= kMax ||
+    // row offsets inside a head are 32-bit (the 16-bit kernels: byte offsets)
+    const int64_t elt = dtype == FA2_DTYPE_F32 ? 1 : 2;
+    if (B >= kMax || H >= kMax || Hk >= kMax || total_q * D * elt >= kMax || total_k * D * elt >= kMax ||
         H * total_q >= kMax)
         return FA2_ERR_UNSUPPORTED;
     int64_t wl = window_left, wr = window_right;
@@ -1144,7 +1566,8 @@ extern "C" int fa2_bwd_varlen(const void* q, const void* k, const void* v, const
     const int64_t n_kt = ceil_div(max_seqlen_k, e->kv_block_n);
     const int64_t n_qt = ceil_div(max_seqlen_q, e->q_block_m);
     if (BH >= kMax || n_kt * BHk >= kMax || n_qt * BH >= kMax) return FA2_ERR_UNSUPPORTED;
-    const size_t q_bytes = (size_t)H * total_q * D * 2, kv_bytes = (size_t)Hk * total_k * D * 2,
+    const size_t eb = dtype == FA2_DTYPE_F32 ? 4 : 2;
+    const size_t q_bytes = (size_t)H * total_q * D * eb, kv_bytes = (size_t)Hk * total_k * D * eb,
                  row_bytes = (size_t)H * total_q * 4;
     if (bwd_outputs_overlap(q, k, v, o, lse, dout, dq, dk, dv, delta, q_bytes, kv_bytes, row_bytes))
         return FA2_ERR_INVALID_ARGUMENT;

@@ -244,11 +244,11 @@ int fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* 
  *   lse             [B, H, M]       float32, the forward's logsumexp output
  *   delta           [B, H, M]       float32 (output): rowsum(dout o o)
  * o and lse must be the forward's outputs for the same q, k, v, scale and
- * causal flag.  dq, dk, dv are rounded to nearest even.
+ * causal flag.  16-bit dq, dk, dv are rounded to nearest even.
  *
  * Arguments as for fa2_fwd_ex (B, H, Hk, M, N >= 1, D, scale, causal, dtype,
- * stream).  This build supports dtype BF16 and F16 with D = 64 or 128; F32
- * returns FA2_ERR_UNSUPPORTED.
+ * stream).  This build supports dtype F32, BF16 and F16 with D = 64 or 128
+ * (F32: fp32 products throughout, P and dS included).
  *
  * Ownership: every buffer is caller-allocated device memory; the library
  * allocates nothing.  The outputs dq, dk, dv and delta must not overlap each

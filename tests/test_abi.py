@@ -230,10 +230,11 @@ def test_bwd_misaligned_pointers_rejected(name, off):
     assert call_bwd(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT
 
 
-def test_bwd_unsupported_dtype_and_head_dim():
-    assert call_bwd(dtype=fa2.FA2_DTYPE_F32) == fa2.FA2_ERR_UNSUPPORTED
-    for D in (32, 96, 256):
-        assert call_bwd(D=D) == fa2.FA2_ERR_UNSUPPORTED
+def test_bwd_unsupported_head_dim_and_sizes():
+    for dtype in (fa2.FA2_DTYPE_BF16, fa2.FA2_DTYPE_F16, fa2.FA2_DTYPE_F32):
+        for D in (32, 96, 256):
+            assert call_bwd(D=D, dtype=dtype) == fa2.FA2_ERR_UNSUPPORTED
+    # the 16-bit kernels address one head's K (V) through a 32-bit byte range
     assert call_bwd(N=1 << 23, D=128) == fa2.FA2_ERR_UNSUPPORTED
 
 
@@ -326,8 +327,8 @@ def test_bwd_local_bad_arguments_rejected(kw):
 
 
 def test_bwd_local_unsupported():
-    assert call_bwd_local(dtype=fa2.FA2_DTYPE_F32) == fa2.FA2_ERR_UNSUPPORTED
     assert call_bwd_local(D=96) == fa2.FA2_ERR_UNSUPPORTED
+    assert call_bwd_local(D=96, dtype=fa2.FA2_DTYPE_F32) == fa2.FA2_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("kw", [dict(cq=0), dict(ck=CK + 1), dict(max_q=17), dict(max_k=-1), dict(total_q=-1),
@@ -337,5 +338,5 @@ def test_bwd_varlen_bad_arguments_rejected(kw):
 
 
 def test_bwd_varlen_unsupported_and_empty():
-    assert call_bwd_varlen(dtype=fa2.FA2_DTYPE_F32) == fa2.FA2_ERR_UNSUPPORTED
+    assert call_bwd_varlen(D=96, dtype=fa2.FA2_DTYPE_F32) == fa2.FA2_ERR_UNSUPPORTED
     assert call_bwd_varlen(B=0, cq=0, ck=0) == fa2.FA2_OK

@@ -174,9 +174,8 @@ WORKLOADS.update({
 })
 WIDENED = ["causal_f16_4k", "gqa_bf16_4k", "decode_gqa_bf16", "swa_bf16_16k", "varlen_bf16_mix"]
 
-# Workloads whose backward pass the bench also times (16-bit only: the
-# backward has no fp32 kernels).
-BACKWARD = ["causal_bf16_4k", "causal_bf16_16k", "ragged_bf16_cross", "gqa_bf16_4k", "causal_f16_4k"]
+# Workloads whose backward pass the bench also times.
+BACKWARD = ["causal_bf16_4k", "causal_bf16_16k", "ragged_bf16_cross", "gqa_bf16_4k", "causal_f16_4k", "mha_f32_2k"]
 
 
 def get(name: str) -> Workload:
