@@ -325,7 +325,7 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     """Gradients of the attention forward on the current CUDA/HIP stream.
 
     q, o, dout: [B,H,M,D]; k, v: [B,Hk,N,D], contiguous device tensors of one
-    dtype (bfloat16 or float16); lse: the forward's [B,H,M] float32 output
+    dtype (float32, bfloat16 or float16); lse: the forward's [B,H,M] float32 output
     for the same inputs, scale and causal flag.  Returns (dq, dk, dv), shaped
     and typed like q, k, v; dk and dv sum over the query heads of each K/V
     head.  ``delta`` ([B,H,M] float32, rowsum(dout * o)) is scratch the call

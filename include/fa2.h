@@ -75,7 +75,10 @@ typedef enum {
  * Ownership: all buffers are allocated and owned by the caller on the
  * current HIP device; the library allocates nothing and keeps no state, so
  * concurrent calls on different streams are safe.  o must not overlap q, k or
- * v, and lse must not overlap any other buffer.
+ * v, and lse must not overlap any other buffer.  Every entry point of this
+ * header only enqueues kernels on `stream` (no allocation, no memset, no
+ * synchronisation), so a call may be captured into a HIP graph and replayed;
+ * the replay reads whatever the captured buffers hold at that time.
  *
  * Runtime: libfa2 needs libamdhip64.so.7.  In a process that already uses a
  * HIP runtime (for instance the copy bundled with PyTorch), load that runtime
