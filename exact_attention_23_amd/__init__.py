@@ -439,8 +439,7 @@ _function = None
 
 def attention(q, k, v, causal: bool = False, scale: float | None = None, window=(-1, -1)):
     """softmax(scale * q k^T) v with autograd: the forward runs fa2_fwd_ex
-    (fa2_fwd_local with a window), the backward fa2_bwd_local (bfloat16 /
-    float16 inputs for the backward)."""
+    (fa2_fwd_local with a window), the backward fa2_bwd_local."""
     global _function
     if _function is None:
         _function = _make_function()

@@ -26,8 +26,10 @@
 //    O and dO);
 //  * the dK/dV kernel gives each workgroup one tile of keys (32 per wave) of
 //    one K/V head and streams the query tiles of every query head of its
-//    group through LDS; K and V of the wave's keys stay in VGPRs, dK and dV
-//    accumulate in registers and are written once -- no atomics;
+//    group through LDS; K and V of the wave's keys stay in VGPRs (at
+//    D = 128 in LDS instead, with two waves per 32 keys: the wave-pair
+//    kernel), dK and dV accumulate in registers and are written once -- no
+//    atomics;
 //  * the dQ kernel gives each workgroup one tile of queries (32 per wave),
 //    keeps Q and dO in VGPRs and streams K/V tiles through LDS, exactly like
 //    the forward; it recomputes P and dP rather than accumulating dQ with
@@ -45,6 +47,8 @@
 // dQ^T += K^T dS^T with K^T read transposed.  Q and dO tiles (dK/dV kernel)
 // and K tiles (dQ kernel) are read both row-wise and transposed, so they use
 // one XOR swizzle that keeps both patterns free of LDS bank conflicts.
+// fp32 inputs run the same schedule on v_mfma_f32_32x32x2_f32 with P and dS
+// kept in fp32 (the fp32 section below).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
