@@ -1,0 +1,26 @@
+"""The C ABI from a plain C program (tests/c/fa2_c_client.c): device buffers
+from the HIP runtime's C API, libfa2's entry points with raw pointers, the
+results checked against the CPU oracle inside that program (fp32 and bf16
+forward with grouped K/V heads, a split-K/V decode forward, an fp32
+backward)."""
+import os
+import subprocess
+
+import pytest
+
+BIN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "fa2_c_client")
+
+
+def test_c_client_binary_is_built():
+    # __graft_entry__.build() compiles it next to its source
+    assert os.path.exists(BIN), "tests/c/fa2_c_client missing: run __graft_entry__.build()"
+
+
+@pytest.mark.gpu
+def test_c_client_matches_the_oracle():
+    print("case C client", flush=True)
+    res = subprocess.run([BIN], capture_output=True, text=True, timeout=120)
+    print(res.stdout)
+    print(res.stderr)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "all cases within tolerance" in res.stdout
