@@ -85,14 +85,17 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // The 16-bit input types share every kernel; they differ only in the MFMA
-// opcode, the conversion that rounds P and O (to nearest even in both), and
-// the packed sum of two rounded weights.
+// opcode, the conversion that rounds P and O (to nearest even in both), the
+// packed sum of two rounded weights and the range a weight may take.
 template <typename E>
 struct Half;
 template <>
 struct Half<__bf16> {
     using v8 = bf16x8;
     using v2 = bf16x2;
+    // largest sum of softmax weights a lane may accept without moving the
+    // running max: every weight is then below it, and bf16 has fp32's range
+    static constexpr float kWeightSumCap = 0x1p32f;
     static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
@@ -105,6 +108,7 @@ template <>
 struct Half<_Float16> {
     using v8 = f16x8;
     using v2 = f16x2;
+    static constexpr float kWeightSumCap = 0x1p15f;  // fp16 ends at 65504
     static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }

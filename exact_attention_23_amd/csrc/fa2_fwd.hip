@@ -426,43 +426,20 @@ fa2_fwd_half_kernel(const FwdParams p) {
         }
 
         V8 pf[T::kKB][2][QB];  // P^T as B operands of the PV MFMAs
-        // Online softmax in the log2 domain.  The running max is only moved
-        // (and O, l rescaled) when some row's max grew by more than 8 (a factor
-        // 256); otherwise P = exp2(s*c - m_run) <= 256, which the fp32 O and l
-        // and the bf16 P hold as accurately -- O / l and m + log2 l are the
-        // same quantities either way.
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            // IEEE maximum (v_maximum3_f32): no NaN quieting of each input
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < T::kKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2)
-                    mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(sacc[kb][qb][r], sacc[kb][qb][r + 1]));
-            {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-                mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            }
-            const float m_tile = mx * c_log2;
-            if (__any(m_tile > m_run[qb] + 8.f)) {
-                // (the empty volatile asm keeps the compiler from turning this
-                // rarely taken branch into an always-executed multiply by a
-                // selected factor)
-                __asm__ volatile("");
-                const float m_new = fmaxf(m_run[qb], m_tile);
-                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run[qb] - m_new);
-                m_run[qb] = m_new;
-                l_run[qb] *= alpha;
-                l_exact[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < T::kDB; ++db) oacc[db][qb] *= alpha;
-            }
-            // P is rounded to bf16 once, for the PV MFMA.  l_run sums exactly
-            // those rounded weights (two per v_dot2 against (1, 1)), so O / l_run
-            // is a true weighted mean of V rows; l_exact sums the fp32 weights,
-            // which L needs to within 1e-3.
-            const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+        // Online softmax in the log2 domain.  The weights are first taken
+        // against the running max as it stands, P = exp2(s*c - m_run); the
+        // max only has to move when some weight would leave the range of the
+        // 16-bit P (and of fp32 O and l), which the lane's sum of P shows
+        // after the fact: a sum above Half<E>::kWeightSumCap, an inf, or the
+        // NaN of a row with no max yet fails the test, and only then is the
+        // tile's row max taken, O and l rescaled and P recomputed.  Large
+        // weights lose nothing (fp32 O and l and the 16-bit P are relative
+        // formats; the key that last set the max had weight 1, so l >= 1).
+        // P is rounded once, for the PV MFMA.  l_run sums exactly those
+        // rounded weights (two per v_dot2 against (1, 1)), so O / l_run is a
+        // true weighted mean of V rows; l_exact sums the fp32 weights, which
+        // L needs to within 1e-3.
+        auto weights = [&](int qb, float m_sub, float& lr, float& le) {
             float lsum = 0.f, esum = 0.f;
 #pragma unroll
             for (int kb = 0; kb < T::kKB; ++kb)
@@ -470,8 +447,8 @@ fa2_fwd_half_kernel(const FwdParams p) {
                 for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
                     for (int t = 0; t < 8; t += 2) {
-                        const float p0 = fast_exp2(fmaf(sacc[kb][qb][8 * ms + t], c_log2, -m_use));
-                        const float p1 = fast_exp2(fmaf(sacc[kb][qb][8 * ms + t + 1], c_log2, -m_use));
+                        const float p0 = fast_exp2(fmaf(sacc[kb][qb][8 * ms + t], c_log2, -m_sub));
+                        const float p1 = fast_exp2(fmaf(sacc[kb][qb][8 * ms + t + 1], c_log2, -m_sub));
                         const V2 pp = {(E)p0, (E)p1};
                         pf[kb][ms][qb][t] = pp[0];
                         pf[kb][ms][qb][t + 1] = pp[1];
@@ -479,8 +456,39 @@ fa2_fwd_half_kernel(const FwdParams p) {
                         esum += p0;
                         esum += p1;
                     }
-            l_run[qb] += lsum;
-            l_exact[qb] += esum;
+            lr = lsum;
+            le = esum;
+        };
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float lr, le;
+            weights(qb, m_run[qb], lr, le);
+            if (__any(!(le <= Half<E>::kWeightSumCap))) {  // (not ">": NaN must fail too)
+                // (the empty volatile asm keeps the compiler from turning this
+                // rarely taken branch into always-executed selects)
+                __asm__ volatile("");
+                // IEEE maximum (v_maximum3_f32): no NaN quieting of each input
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2)
+                        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(sacc[kb][qb][r], sacc[kb][qb][r + 1]));
+                {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                    mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                }
+                const float m_new = fmaxf(m_run[qb], mx * c_log2);
+                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run[qb] - m_new);
+                m_run[qb] = m_new;
+                l_run[qb] *= alpha;
+                l_exact[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db) oacc[db][qb] *= alpha;
+                weights(qb, m_new == -INFINITY ? 0.f : m_new, lr, le);
+            }
+            l_run[qb] += lr;
+            l_exact[qb] += le;
         }
 
         // O^T += V^T P^T: two 16-key MFMA steps per 32-key block; each A
@@ -717,7 +725,10 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
     // (the scheduling fences keep the compiler from sinking the reads next
     // to their uses).  PV(-1) multiplies a zero P by a zero-filled V buffer;
     // the S(n_w) of a wave's last MFMA phase is computed and discarded, so
-    // every phase runs the same straight-line code.
+    // every phase runs the same straight-line code.  After its MFMAs the
+    // phase adds the rounded weights of P(t-1) to l_run (two per v_dot2
+    // against (1, 1)): work taken out of the softmax phase, which sets the
+    // period, and done while the partner wave issues no MFMAs.
     constexpr int kSteps = T::kDS * T::kKB;  // == number of PV MFMAs
     static_assert(kSteps == T::kKB * 2 * T::kDB, "one PV and one S MFMA per step");
     auto read_v = [&](const char* vprev, int i) {
@@ -760,15 +771,53 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        float ls0 = l_run, ls1 = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                for (int u = 0; u < 8; u += 2) {
+                    const V2 pp = {pf[kb][ms][u], pf[kb][ms][u + 1]};
+                    if ((u >> 1) & 1) ls1 = Half<E>::sum2(pp, ls1);
+                    else ls0 = Half<E>::sum2(pp, ls0);
+                }
+        l_run = ls0 + ls1;
     };
 
     // ---- VALU phase: mask (boundary tiles), online softmax, rescale.
-    // The running max only moves when some row's max grew by more than 8 (a
-    // factor 256); otherwise P = exp2(s*c - m_run) <= 256, which the fp32 O
-    // and l and the bf16 P hold as accurately.  P is rounded to bf16 once;
-    // l_run sums those rounded weights (two per v_dot2 against (1, 1)) so
-    // O / l_run is a true weighted mean of V rows, and l_exact sums the fp32
-    // weights for L.
+    // The weights are first taken against the running max as it stands,
+    // P = exp2(s*c - m_run), with no max of the tile: the max only has to
+    // move when some weight would leave the range of the 16-bit P (and of
+    // fp32 O and l), and the lane's sum of P shows that after the fact: a
+    // sum above Half<E>::kWeightSumCap (2^32 for bf16, 2^15 for fp16), an
+    // inf, or the NaN of a row with no max yet fails the test.  Only then
+    // is the tile's row max taken, O and l rescaled and P recomputed.  So
+    // after a row's first tile the max moves only when its scores jump by
+    // more than about 27 (bf16) or 10 (fp16) in log2 units, and the common
+    // tile runs no max reduction ahead of its exponentials.  Large weights
+    // lose nothing: fp32 O and l and the 16-bit P are relative formats, and
+    // the weight of the key that last set the max was 1, so l >= 1 and tiny
+    // weights stay negligible.  P is rounded once; l_exact sums the fp32
+    // weights (for L), l_run the rounded ones (in the MFMA phase that
+    // consumes P).
+    auto weights = [&](float m_sub) {
+        float esum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                for (int u = 0; u < 8; u += 2) {
+                    const float p0 = fast_exp2(fmaf(sacc[kb][8 * ms + u], c_log2, -m_sub));
+                    const float p1 = fast_exp2(fmaf(sacc[kb][8 * ms + u + 1], c_log2, -m_sub));
+                    const V2 pp = {(E)p0, (E)p1};
+                    pf[kb][ms][u] = pp[0];
+                    pf[kb][ms][u + 1] = pp[1];
+                    esum[(u >> 1) & 3] += p0 + p1;
+                }
+        return (esum[0] + esum[1]) + (esum[2] + esum[3]);
+    };
     auto valu_phase = [&](int t) {
         if (t < 0 || t >= n_w) return;
         const int kbase = (kv_t0 + t) * BN;
@@ -783,52 +832,34 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
                 for (int r = 0; r < 16; ++r)
                     if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
         }
-        // row max as four independent v_maximum3 chains, then a short tree
-        float mxp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-        for (int kb = 0; kb < T::kKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                float& m4 = mxp[((kb * 16 + r) >> 1) & 3];
-                m4 = __builtin_elementwise_maximum(m4, __builtin_elementwise_maximum(sacc[kb][r], sacc[kb][r + 1]));
-            }
-        float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mxp[0], mxp[1]),
-                                                 __builtin_elementwise_maximum(mxp[2], mxp[3]));
-        {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const float m_tile = mx * c_log2;
-        if (__any(m_tile > m_run + 8.f)) {
+        float e_tile = weights(m_run);
+        if (__any(!(e_tile <= Half<E>::kWeightSumCap))) {  // (not ">": NaN must fail too)
             __asm__ volatile("");
-            const float m_new = fmaxf(m_run, m_tile);
+            // row max as four independent v_maximum3 chains, then a short tree
+            float mxp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+            for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    float& m4 = mxp[((kb * 16 + r) >> 1) & 3];
+                    m4 = __builtin_elementwise_maximum(m4, __builtin_elementwise_maximum(sacc[kb][r], sacc[kb][r + 1]));
+                }
+            float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mxp[0], mxp[1]),
+                                                     __builtin_elementwise_maximum(mxp[2], mxp[3]));
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            const float m_new = fmaxf(m_run, mx * c_log2);
             const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
             l_exact *= alpha;
 #pragma unroll
             for (int db = 0; db < T::kDB; ++db) oacc[db] *= alpha;
+            e_tile = weights(m_run == -INFINITY ? 0.f : m_run);
         }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        // partial sums in four independent chains each (no serial add chain)
-        float lsum[4] = {0.f, 0.f, 0.f, 0.f}, esum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < T::kKB; ++kb)
-#pragma unroll
-            for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-                for (int u = 0; u < 8; u += 2) {
-                    const int c = (u >> 1) & 3;
-                    const float p0 = fast_exp2(fmaf(sacc[kb][8 * ms + u], c_log2, -m_use));
-                    const float p1 = fast_exp2(fmaf(sacc[kb][8 * ms + u + 1], c_log2, -m_use));
-                    const V2 pp = {(E)p0, (E)p1};
-                    pf[kb][ms][u] = pp[0];
-                    pf[kb][ms][u + 1] = pp[1];
-                    lsum[c] = Half<E>::sum2(pp, lsum[c]);
-                    esum[c] += p0 + p1;
-                }
-        l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-        l_exact += (esum[0] + esum[1]) + (esum[2] + esum[3]);
+        l_exact += e_tile;
     };
 
     // ---- prologue: K_0 in buffer 0; V buffer 1 zeroed (read by PV(-1))

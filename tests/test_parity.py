@@ -149,6 +149,30 @@ def test_large_magnitude_scores():
     check_case(2, 2, 333, 777, 128, "f16", False, seed=13, qk_sigma=4.0)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_running_max_jumps_late(D, causal, dtype):
+    # Keys planted deep into the sequence as 2, 8 and 16 times a late query
+    # row: that row's max (scaled scores in log2 units) grows from ~4 in its
+    # first tile to ~27, ~110 and ~220 long after it, the last past fp32's
+    # exp range, and the other rows see scores of std up to ~28 at those
+    # keys.  The running max and the rescale of O and l must follow
+    # every jump, small or large.
+    B, H, M, N = 1, 2, 700, 1000
+    what = f"max jumps D={D} {dtype} causal={causal}"
+    note("case " + what)
+    q, k, v = workloads.make_inputs(B, H, M, N, D, dtype, seed=31 + D)
+    target = M - 5
+    for key, factor in ((150, 2.0), (420, 8.0), (690, 16.0)):
+        # powers of two keep the planted keys exact in every dtype
+        k[:, :, key] = q[:, :, target] * factor
+    o, lse = run_gpu(q, k, v, causal)
+    o_ref, l_ref = oracle.attention(q, k, v, 1.0 / math.sqrt(D), causal)
+    assert l_ref[0, 0, target] > 125, "the planted key dominates the target row"
+    compare(o, lse, o_ref, l_ref, dtype, what)
+
+
 # ------------------------------------------------------ closed-form examples
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
