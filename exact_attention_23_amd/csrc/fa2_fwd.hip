@@ -941,6 +941,9 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
 // fp32 kernel (v_mfma_f32_32x32x2_f32: true fp32 products, no reduced-precision
 // shortcut)
 // ---------------------------------------------------------------------------
+// K and V tiles are copied global -> LDS by the load unit as in the 16-bit
+// kernels (16 bytes per lane, no VGPR staging, unpadded rows whose 16-byte
+// chunks are XOR-swizzled), which keeps the registers free for Q, O and S.
 template <int D, int BN, int NW>
 struct F32Traits {
     static constexpr int kThreads = NW * 64;
@@ -948,18 +951,26 @@ struct F32Traits {
     static constexpr int kKB = BN / 32;
     static constexpr int kDB = D / 32;
     static constexpr int kHalfD = D / 2;          // d values per lane half
-    static constexpr int kKStr = D + 4;           // floats
-    static constexpr int kVStr = D + 8;           // floats
-    static constexpr int kKElems = BN * kKStr;
-    static constexpr int kVElems = BN * kVStr;
-    static constexpr int kChunks = BN * D / 4;    // 16-byte chunks per tile
-    static constexpr int kPerThread = kChunks / kThreads;
-    static_assert(kChunks % kThreads == 0, "loader split");
-    static constexpr size_t kLdsBytes = 2 * (kKElems + kVElems) * sizeof(float);
+    static constexpr int kRowBytes = D * 4;
+    static constexpr int kCPR = D / 4;            // 16-byte chunks per row
+    static constexpr int kTileBytes = BN * kRowBytes;
+    static constexpr int kTileChunks = BN * kCPR;
+    static constexpr int kLoadsPerWave = kTileChunks / (64 * NW);  // per tensor per tile
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(kTileChunks % (64 * NW) == 0, "loader split");
 };
 
+// Chunk XORs of the fp32 tiles.  K: a quarter-wave reads one logical chunk
+// (4 floats of d) of 16 consecutive rows; XOR with the row's low 4 bits puts
+// them in 16 distinct bank groups.  V: lanes 0-31 read 32 floats of d (8
+// chunks) of key row r and lanes 32-63 the same d of row r + 4 (bit 2 of the
+// row is the lane half); XOR 8 moves the second row's 8 chunks to the other
+// half of the bank space.
+__device__ __forceinline__ int swz_k_f32(int r) { return r & 15; }
+__device__ __forceinline__ int swz_v_f32(int r) { return 8 * ((r >> 2) & 1); }
+
 template <int D, int BN, int NW, int MASK, bool SPLIT>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64, 2)
 fa2_fwd_f32_kernel(const FwdParams p) {
     using T = F32Traits<D, BN, NW>;
     const float* __restrict__ Q = static_cast<const float*>(p.q);
@@ -968,8 +979,10 @@ fa2_fwd_f32_kernel(const FwdParams p) {
     float* __restrict__ O = static_cast<float*>(p.o);
     float* __restrict__ LSE = p.lse;
     const float c_log2 = p.c_log2;
-    __shared__ __attribute__((aligned(16))) float sK[2][T::kKElems];
-    __shared__ __attribute__((aligned(16))) float sV[2][T::kVElems];
+    __shared__ __attribute__((aligned(1024))) char sK0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK1[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV1[T::kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1009,110 +1022,125 @@ fa2_fwd_f32_kernel(const FwdParams p) {
     for (int db = 0; db < T::kDB; ++db) oacc[db] = floatx16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    u32x4 kreg[T::kPerThread], vreg[T::kPerThread];
-    auto load_tile = [&](int kt) {
-        const int kbase = (kv_t0 + kt) * BN;
+    // ---- async tile copies: wave w moves chunks [w*L*64, (w+1)*L*64) of each
+    // tensor's tile; LDS slot s holds row s / CPR, physical chunk s % CPR,
+    // i.e. logical chunk (s % CPR) ^ swz(row).
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t cp_koff[T::kLoadsPerWave], cp_voff[T::kLoadsPerWave];
 #pragma unroll
-        for (int i = 0; i < T::kPerThread; ++i) {
-            const int id = tid + i * T::kThreads;
-            const int row = id / (D / 4);
-            const int c4 = id % (D / 4);
-            const int key = kbase + row;
-            const bool ok = key < N;
-            kreg[i] = ok ? *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + 4 * c4) : u32x4{0, 0, 0, 0};
-            vreg[i] = ok ? *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + 4 * c4) : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < T::kPerThread; ++i) {
-            const int id = tid + i * T::kThreads;
-            const int row = id / (D / 4);
-            const int c4 = id % (D / 4);
-            *reinterpret_cast<u32x4*>(&sK[buf][row * T::kKStr + 4 * c4]) = kreg[i];
-            *reinterpret_cast<u32x4*>(&sV[buf][row * T::kVStr + 4 * c4]) = vreg[i];
-        }
-    };
-
-    if (n_kv > 0) {
-        load_tile(0);
-        store_tile(0);
+    for (int i = 0; i < T::kLoadsPerWave; ++i) {
+        const int slot = (wave * T::kLoadsPerWave + i) * 64 + lane;
+        const int r = slot / T::kCPR, c = slot % T::kCPR;
+        cp_koff[i] = (uint32_t)(r * T::kRowBytes + 16 * (c ^ swz_k_f32(r)));
+        cp_voff[i] = (uint32_t)(r * T::kRowBytes + 16 * (c ^ swz_v_f32(r)));
     }
-    __syncthreads();
+    auto issue_tile = [&](int kt, char* kdst, char* vdst) {
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Kh, cp_koff, wave_u, kv_t0 + kt, N, kdst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Vh, cp_voff, wave_u, kv_t0 + kt, N, vdst);
+    };
 
-    for (int kt = 0; kt < n_kv; ++kt) {
-        const int buf = kt & 1;
-        const bool has_next = kt + 1 < n_kv;
-        if (has_next) load_tile(kt + 1);
+    // per-lane parts of the LDS operand addresses: K row l32 (of each 32-row
+    // block) at logical chunk h*D/8 + s/4; V element (row, d = 32 db + l32)
+    // of rows whose bit 2 is h
+    const int k_lane = l32 * T::kRowBytes;
+    const int k_swz = swz_k_f32(l32);
+    int v_lane_off[T::kDB];
+#pragma unroll
+    for (int db = 0; db < T::kDB; ++db)
+        v_lane_off[db] = 16 * ((8 * db + (l32 >> 2)) ^ (8 * h)) + 4 * (l32 & 3);
 
-        if (kt >= wtiles.first && kt < wtiles.end) {
-            const float* kt_lds = sK[buf];
-            const float* vt_lds = sV[buf];
-
-            floatx16 sacc[T::kKB];
+    // (always inlined: an out-of-line call would keep O, S and Q in memory)
+    auto compute_tile = [&](int kt, const char* klds, const char* vlds) __attribute__((always_inline)) {
+        floatx16 sacc[T::kKB];
 #pragma unroll
-            for (int kb = 0; kb < T::kKB; ++kb) sacc[kb] = floatx16{};
+        for (int kb = 0; kb < T::kKB; ++kb) sacc[kb] = floatx16{};
 #pragma unroll
-            for (int kb = 0; kb < T::kKB; ++kb) {
-                const float* krow = kt_lds + (32 * kb + l32) * T::kKStr + h * T::kHalfD;
+        for (int kb = 0; kb < T::kKB; ++kb) {
+            const char* krow = klds + 32 * kb * T::kRowBytes + k_lane;
 #pragma unroll
-                for (int s = 0; s < T::kHalfD; s += 4) {
-                    const floatx4 kf = *reinterpret_cast<const floatx4*>(krow + s);
+            for (int s = 0; s < T::kHalfD; s += 4) {
+                const int c = h * (T::kHalfD / 4) + s / 4;
+                const floatx4 kf = *reinterpret_cast<const floatx4*>(krow + 16 * (c ^ k_swz));
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[u], qf[s + u], sacc[kb], 0, 0, 0);
-                }
+                for (int u = 0; u < 4; ++u)
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[u], qf[s + u], sacc[kb], 0, 0, 0);
             }
+        }
 
-            const int kbase = (kv_t0 + kt) * BN;
-            if (tile_needs_mask<MASK>(p, kbase, BN, N, qw0, qw1)) {
-                const int query = qw0 + l32;
-                const int hi = key_hi<MASK>(p, query, N), lo = key_lo<MASK>(p, query);
-#pragma unroll
-                for (int kb = 0; kb < T::kKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kbase + 32 * kb + acc_row(r, h);
-                        if (key > hi || key < lo) sacc[kb][r] = -INFINITY;
-                    }
-            }
-
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < T::kKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = fmaxf(mx, xchg_half(mx));
-            const float m_new = fmaxf(m_run, mx * c_log2);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
-            m_run = m_new;
-            float lsum = 0.f;
+        const int kbase = (kv_t0 + kt) * BN;
+        if (tile_needs_mask<MASK>(p, kbase, BN, N, qw0, qw1)) {
+            const int query = qw0 + l32;
+            const int hi = key_hi<MASK>(p, query, N), lo = key_lo<MASK>(p, query);
 #pragma unroll
             for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(fmaf(sacc[kb][r], c_log2, -m_use));
-                    sacc[kb][r] = p;
-                    lsum += p;
+                    const int key = kbase + 32 * kb + acc_row(r, h);
+                    if (key > hi || key < lo) sacc[kb][r] = -INFINITY;
                 }
-            l_run = fmaf(l_run, alpha, lsum);
+        }
+
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        mx = fmaxf(mx, xchg_half(mx));
+        // The running max moves (and O, l are rescaled) only when some row's
+        // max grew by more than 8 in log2 units; otherwise the weights stay
+        // below 2^8, which fp32 holds as accurately.
+        const float m_tile = mx * c_log2;
+        if (__any(m_tile > m_run + 8.f)) {
+            __asm__ volatile("");  // a rarely taken branch, not selects
+            const float m_new = fmaxf(m_run, m_tile);
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < T::kDB; ++db) oacc[db] *= alpha;
-
-            // O^T += V^T P^T: MFMA step r contracts key acc_row(r, h) in each half
-#pragma unroll
-            for (int kb = 0; kb < T::kKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float* vrow = vt_lds + (32 * kb + acc_row(r, h)) * T::kVStr + l32;
-#pragma unroll
-                    for (int db = 0; db < T::kDB; ++db)
-                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * db], sacc[kb][r], oacc[db], 0, 0, 0);
-                }
         }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pw = fast_exp2(fmaf(sacc[kb][r], c_log2, -m_use));
+                sacc[kb][r] = pw;
+                lsum += pw;
+            }
+        l_run += lsum;
 
-        if (has_next) store_tile(buf ^ 1);
+        // O^T += V^T P^T: MFMA step r contracts key acc_row(r, h) in each half
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const char* vrow = vlds + (32 * kb + acc_row(r, 0)) * T::kRowBytes + 4 * h * T::kRowBytes;
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        *reinterpret_cast<const float*>(vrow + v_lane_off[db]), sacc[kb][r], oacc[db], 0, 0, 0);
+            }
+    };
+
+    // ---- main loop, unrolled by two over the buffer pair so that every LDS
+    // access names its buffer (the copy in flight never aliases the one read)
+    if (n_kv > 0) issue_tile(0, sK0, sV0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    auto run_tile = [&](int kt, const char* klds, const char* vlds) __attribute__((always_inline)) {
+        if (kt >= wtiles.first && kt < wtiles.end) compute_tile(kt, klds, vlds);
+    };
+    for (int kt = 0; kt < n_kv; kt += 2) {
+        if (kt + 1 < n_kv) issue_tile(kt + 1, sK1, sV1);
+        run_tile(kt, sK0, sV0);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
+        __syncthreads();
+        if (kt + 1 >= n_kv) break;
+        if (kt + 2 < n_kv) issue_tile(kt + 2, sK0, sV0);
+        run_tile(kt + 1, sK1, sV1);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
