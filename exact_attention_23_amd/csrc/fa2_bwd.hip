@@ -954,11 +954,15 @@ fa2_bwd_dq_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 // MFMA step s of a product over d contracts d = h D/2 + s in lane half h of
 // both operands (as in the fp32 forward), so a lane reads four consecutive
-// d of a row at once; step r of a product over the rows of a 32-row block
-// contracts rows acc_row(r, 0) and acc_row(r, 1), the rows whose P (or dS)
-// the lane's accumulator register r holds.  Tiles live in LDS as fp32 rows
-// padded to D + 4 floats: 16 consecutive rows read at one d then start 4
-// banks apart.
+// d of a row at once (row-wise reads: 16 consecutive rows at one 16-byte
+// chunk per quarter-wave); step r of a product over the rows of a 32-row
+// block contracts rows acc_row(r, 0) and acc_row(r, 1), the rows whose P (or
+// dS) the lane's accumulator register r holds (column reads: 32 floats of d
+// of row r in lanes 0-31 and of row r + 4 in lanes 32-63).  Streamed tiles
+// reach LDS by direct buffer-to-LDS copies into unpadded rows whose 16-byte
+// chunks are XORed with swz_f32b(row): its low 4 bits spread the row-wise
+// reads over 16 bank groups, and its bit 3 (row bit 3 ^ row bit 2) puts rows
+// r and r + 4 in opposite halves of the bank space for the column reads.
 
 // Delta = rowsum(dO o O): D / 4 lanes per row, 16 bytes each.
 template <int D>
@@ -990,46 +994,80 @@ struct BwdF32Traits {
     static constexpr int kBlock = 32 * kNW;           // keys (dK/dV) or queries (dQ) per workgroup
     static constexpr int kDB = D / 32;
     static constexpr int kHalfD = D / 2;
-    static constexpr int kStr = D + 4;                // floats per LDS row
-    static constexpr int kTileElems = kRows * kStr;
-    static constexpr int kChunks = kRows * D / 4;     // 16-byte chunks per tile
-    static constexpr int kPerThread = kChunks / kThreads;
+    static constexpr int kRowBytes = D * 4;
+    static constexpr int kCPR = D / 4;                // 16-byte chunks per row
+    static constexpr int kTileBytes = kRows * kRowBytes;
+    static constexpr int kLoadsPerWave = kRows * kCPR / (64 * kNW);  // per tensor per tile
+    // two waves per SIMD at D = 64; at D = 128 the wave's K, V (Q, dO) rows
+    // and its two accumulators alone take 256 registers
+    static constexpr int kWavesPerSimd = D == 64 ? 2 : 1;
     static_assert(D == 64 || D == 128, "head dim");
-    static_assert(kChunks % kThreads == 0, "loader split");
+    static_assert((kRows * kCPR) % (64 * kNW) == 0, "loader split");
 };
 
-// Rows [row0, row0 + 32) of a head's [rows, D] fp32 matrix through registers
-// into an LDS tile; rows at or past `n` are zero.
+__device__ __forceinline__ int swz_f32b(int r) { return (r & 15) ^ (8 * ((r >> 2) & 1)); }
+
+// This lane's byte offsets inside a streamed tile (row * row bytes +
+// swizzled chunk): wave w moves chunks [w*L*64, (w+1)*L*64), LDS slot s holds
+// row s / CPR, physical chunk s % CPR.
 template <int D>
-struct F32TileLoader {
+struct F32Stream {
     using T = BwdF32Traits<D>;
-    u32x4 a[T::kPerThread], b[T::kPerThread];
-    __device__ __forceinline__ void load(const float* A, const float* B, int row0, int n, int tid) {
+    uint32_t off[T::kLoadsPerWave];
+    __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-        for (int i = 0; i < T::kPerThread; ++i) {
-            const int id = tid + i * T::kThreads;
-            const int r = row0 + id / (D / 4), c4 = id % (D / 4);
-            const bool ok = r < n;
-            a[i] = ok ? *reinterpret_cast<const u32x4*>(A + (int64_t)r * D + 4 * c4) : u32x4{0, 0, 0, 0};
-            b[i] = ok ? *reinterpret_cast<const u32x4*>(B + (int64_t)r * D + 4 * c4) : u32x4{0, 0, 0, 0};
-        }
-    }
-    __device__ __forceinline__ void store(float* sa, float* sb, int tid) const {
-#pragma unroll
-        for (int i = 0; i < T::kPerThread; ++i) {
-            const int id = tid + i * T::kThreads;
-            const int r = id / (D / 4), c4 = id % (D / 4);
-            *reinterpret_cast<u32x4*>(sa + r * T::kStr + 4 * c4) = a[i];
-            *reinterpret_cast<u32x4*>(sb + r * T::kStr + 4 * c4) = b[i];
+        for (int i = 0; i < T::kLoadsPerWave; ++i) {
+            const int slot = (wave * T::kLoadsPerWave + i) * 64 + lane;
+            const int r = slot / T::kCPR, c = slot % T::kCPR;
+            off[i] = (uint32_t)(r * T::kRowBytes + 16 * (c ^ swz_f32b(r)));
         }
     }
 };
+
+// Row-wise operand: floats d = h D/2 + s .. + 3 of row l32 (s % 4 == 0); `lane_row`
+// is l32 * row bytes, `lane_xor` the lane's part of the chunk index XOR.
+template <int D>
+__device__ __forceinline__ floatx4 f32_row_read(const char* tile, int lane_row, int lane_xor, int s) {
+    return *reinterpret_cast<const floatx4*>(tile + lane_row + 16 * (lane_xor ^ (s / 4)));
+}
+// Column operand of step r, block db: d = 32 db + l32 of row acc_row(r, h);
+// `col_lane[db]` holds the lane's part (row 4h, chunk and in-chunk offset).
+template <int D>
+__device__ __forceinline__ float f32_col_read(const char* tile, const int* col_lane, int r, int db) {
+    constexpr int kRowBytes = D * 4;
+    const int rbase = (8 * (r >> 2) + (r & 3)) * kRowBytes;
+    const int kx = 16 * ((r & 3) | (8 * ((r >> 2) & 1)));
+    return *reinterpret_cast<const float*>(tile + rbase + (col_lane[db] ^ kx));
+}
+// The lane parts of the two reads.  Row-wise: chunk (h D/8 + s/4) ^ swz(l32)
+// = (h D/8 ^ swz(l32)) ^ s/4.  Column: row acc_row(r, h) = 8(r>>2) + 4h +
+// (r&3), whose swz is ((r&3) | 8((r>>2)&1)) ^ 12h, so the chunk
+// (8 db + l32/4) ^ swz splits into a lane part and a step constant.
+// The XORs make every operand address a lane value combined with a step
+// constant, which the compiler would hoist out of the tile loop into one
+// register per address; passing the lane values through an empty asm at the
+// top of each tile keeps them in a few registers and costs one VALU per read.
+template <int N>
+__device__ __forceinline__ void opaque_lanes(int& a, int* b) {
+    __asm__ volatile("" : "+v"(a));
+#pragma unroll
+    for (int i = 0; i < N; ++i) __asm__ volatile("" : "+v"(b[i]));
+}
+template <int D>
+__device__ __forceinline__ void f32_read_lanes(int l32, int h, int& lane_row, int& lane_xor, int* col_lane) {
+    constexpr int kRowBytes = D * 4;
+    lane_row = l32 * kRowBytes;
+    lane_xor = (h * (D / 8)) ^ swz_f32b(l32);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+        col_lane[db] = 4 * h * kRowBytes + 16 * ((8 * db + (l32 >> 2)) ^ (12 * h)) + 4 * (l32 & 3);
+}
 
 // dK, dV: one workgroup of 4 waves per (128-key tile, K/V head); each wave
 // owns 32 keys and keeps their K and V rows in registers; Q and dO stream
 // through LDS 32 rows at a time.
 template <int D, int MASK>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, BwdF32Traits<D>::kWavesPerSimd)
 fa2_bwd_dkdv_f32_kernel(const BwdParams p) {
     using T = BwdF32Traits<D>;
     const float* __restrict__ Q = static_cast<const float*>(p.q);
@@ -1039,9 +1077,11 @@ fa2_bwd_dkdv_f32_kernel(const BwdParams p) {
     float* __restrict__ dK = static_cast<float*>(p.dk);
     float* __restrict__ dV = static_cast<float*>(p.dv);
     const float c_log2 = p.c_log2;
-    __shared__ __attribute__((aligned(16))) float sQ[2][T::kTileElems];
-    __shared__ __attribute__((aligned(16))) float sO[2][T::kTileElems];
-    __shared__ __attribute__((aligned(16))) float sL[2][T::kRows], sD[2][T::kRows];
+    __shared__ __attribute__((aligned(1024))) char sQ0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sO0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sQ1[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sO1[T::kTileBytes];
+    __shared__ __attribute__((aligned(16))) float sL0[T::kRows], sD0[T::kRows], sL1[T::kRows], sD1[T::kRows];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1093,41 +1133,50 @@ fa2_bwd_dkdv_f32_kernel(const BwdParams p) {
         qt = qt0 + (it - g * per_g);
         bh = bkv * p.G + g;
     };
-    F32TileLoader<D> ld;
-    float ld_next = 0.f;  // the next tile's L (log2 units, wave 0) or Delta (wave 1) of row `lane`
-    auto fetch = [&](int it) {
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    F32Stream<D> st;
+    st.init(wave, lane);
+    int lane_row, lane_xor, col_lane[T::kDB];
+    f32_read_lanes<D>(l32, h, lane_row, lane_xor, col_lane);
+
+    // Q and dO rows of query tile `it` into LDS (rows past M re-read row M-1;
+    // their L is +inf, so P = dS = 0 there); wave 0 loads the tile's L (log2
+    // units), wave 1 its Delta, into a register until the tile's buffer is free
+    float ld_next = 0.f;
+    auto issue = [&](int it, char* qdst, char* odst) __attribute__((always_inline)) {
         int bh, qt;
         tile_head(it, bh, qt);
         const int64_t qr = q_row0(p, sq, bh);
-        ld.load(Q + qr * D, dO + qr * D, qt * T::kRows, M, tid);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, T::kRows>(Q + qr * D, st.off, wave_u, qt, M, qdst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, T::kRows>(dO + qr * D, st.off, wave_u, qt, M, odst);
         const int row = qt * T::kRows + lane;
         if (wave == 0) ld_next = l2_of(row < M ? p.lse[qr + row] : INFINITY);
         else if (wave == 1) ld_next = row < M ? p.delta[qr + row] : 0.f;
     };
-    auto stash = [&](int buf) {
-        ld.store(sQ[buf], sO[buf], tid);
+    auto stash = [&](float* sl, float* sd) __attribute__((always_inline)) {
         if (lane < T::kRows) {
-            if (wave == 0) sL[buf][lane] = ld_next;
-            else if (wave == 1) sD[buf][lane] = ld_next;
+            if (wave == 0) sl[lane] = ld_next;
+            else if (wave == 1) sd[lane] = ld_next;
         }
     };
 
-    auto compute_tile = [&](int it, int buf) {
+    auto compute_tile = [&](int it, const char* qs, const char* os, const float* sl, const float* sd)
+                            __attribute__((always_inline)) {
         int bh, qt;
         tile_head(it, bh, qt);
         const int r0 = qt * T::kRows;
         if (!block_live<MASK>(p, r0, k0, M, N)) return;
-        const float* qs = sQ[buf];
-        const float* os = sO[buf];
+        int lx = lane_xor, cl[T::kDB];
+#pragma unroll
+        for (int db = 0; db < T::kDB; ++db) cl[db] = col_lane[db];
+        opaque_lanes<T::kDB>(lx, cl);
         // S = Q K^T and dP = dO V^T (rows: the tile's queries, columns: the
         // wave's keys)
         floatx16 sacc = floatx16{}, pacc = floatx16{};
-        const float* qrow = qs + l32 * T::kStr + h * T::kHalfD;
-        const float* orow = os + l32 * T::kStr + h * T::kHalfD;
 #pragma unroll
         for (int s = 0; s < T::kHalfD; s += 4) {
-            const floatx4 qa = *reinterpret_cast<const floatx4*>(qrow + s);
-            const floatx4 oa = *reinterpret_cast<const floatx4*>(orow + s);
+            const floatx4 qa = f32_row_read<D>(qs, lane_row, lx, s);
+            const floatx4 oa = f32_row_read<D>(os, lane_row, lx, s);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[u], kf[s + u], sacc, 0, 0, 0);
@@ -1142,8 +1191,8 @@ fa2_bwd_dkdv_f32_kernel(const BwdParams p) {
         // r0 + acc_row(r, h)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const floatx4 l4 = *reinterpret_cast<const floatx4*>(&sL[buf][8 * g + 4 * h]);
-            const floatx4 d4 = *reinterpret_cast<const floatx4*>(&sD[buf][8 * g + 4 * h]);
+            const floatx4 l4 = *reinterpret_cast<const floatx4*>(&sl[8 * g + 4 * h]);
+            const floatx4 d4 = *reinterpret_cast<const floatx4*>(&sd[8 * g + 4 * h]);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float pv = fast_exp2(fmaf(sacc[4 * g + u], c_log2, -l4[u]));
@@ -1155,26 +1204,33 @@ fa2_bwd_dkdv_f32_kernel(const BwdParams p) {
         // P and dS the lane's register r holds
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = acc_row(r, h);
 #pragma unroll
             for (int db = 0; db < T::kDB; ++db) {
-                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(os[row * T::kStr + 32 * db + l32], sacc[r], dvacc[db], 0, 0, 0);
-                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[row * T::kStr + 32 * db + l32], pacc[r], dkacc[db], 0, 0, 0);
+                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(f32_col_read<D>(os, cl, r, db), sacc[r], dvacc[db], 0, 0, 0);
+                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(f32_col_read<D>(qs, cl, r, db), pacc[r], dkacc[db], 0, 0, 0);
             }
         }
     };
 
+    // ---- main loop, unrolled by two over the buffer pair so that every LDS
+    // access names its buffer (the copy in flight never aliases the one read)
     if (n_it > 0) {
-        fetch(0);
-        stash(0);
+        issue(0, sQ0, sO0);
+        stash(sL0, sD0);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int it = 0; it < n_it; ++it) {
-        const int buf = it & 1;
-        const bool has_next = it + 1 < n_it;
-        if (has_next) fetch(it + 1);
-        compute_tile(it, buf);
-        if (has_next) stash(buf ^ 1);
+    for (int it = 0; it < n_it; it += 2) {
+        if (it + 1 < n_it) issue(it + 1, sQ1, sO1);
+        compute_tile(it, sQ0, sO0, sL0, sD0);
+        if (it + 1 < n_it) stash(sL1, sD1);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
+        __syncthreads();
+        if (it + 1 >= n_it) break;
+        if (it + 2 < n_it) issue(it + 2, sQ0, sO0);
+        compute_tile(it + 1, sQ1, sO1, sL1, sD1);
+        if (it + 2 < n_it) stash(sL0, sD0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
@@ -1202,7 +1258,7 @@ fa2_bwd_dkdv_f32_kernel(const BwdParams p) {
 // owns 32 queries and keeps their Q and dO rows in registers; K and V stream
 // through LDS 32 keys at a time.
 template <int D, int MASK>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, BwdF32Traits<D>::kWavesPerSimd)
 fa2_bwd_dq_f32_kernel(const BwdParams p) {
     using T = BwdF32Traits<D>;
     const float* __restrict__ Q = static_cast<const float*>(p.q);
@@ -1211,8 +1267,10 @@ fa2_bwd_dq_f32_kernel(const BwdParams p) {
     const float* __restrict__ dO = static_cast<const float*>(p.dout);
     float* __restrict__ dQ = static_cast<float*>(p.dq);
     const float c_log2 = p.c_log2;
-    __shared__ __attribute__((aligned(16))) float sK[2][T::kTileElems];
-    __shared__ __attribute__((aligned(16))) float sV[2][T::kTileElems];
+    __shared__ __attribute__((aligned(1024))) char sK0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV0[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK1[T::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV1[T::kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1278,23 +1336,33 @@ fa2_bwd_dq_f32_kernel(const BwdParams p) {
 #pragma unroll
     for (int db = 0; db < T::kDB; ++db) dqacc[db] = floatx16{};
 
-    F32TileLoader<D> ld;
     const float* Kh = K + kvr * D;
     const float* Vh = V + kvr * D;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    F32Stream<D> st;
+    st.init(wave, lane);
+    int lane_row, lane_xor, col_lane[T::kDB];
+    f32_read_lanes<D>(l32, h, lane_row, lane_xor, col_lane);
+    // K and V rows of key tile t0 + kt into LDS (rows past N re-read row
+    // N-1; those keys are masked)
+    auto issue = [&](int kt, char* kdst, char* vdst) __attribute__((always_inline)) {
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Kh, st.off, wave_u, t0 + kt, N, kdst);
+        copy_tile_to_lds<T::kLoadsPerWave, T::kRowBytes, BN>(Vh, st.off, wave_u, t0 + kt, N, vdst);
+    };
 
-    auto compute_tile = [&](int kt, int buf) {
+    auto compute_tile = [&](int kt, const char* ks, const char* vs) __attribute__((always_inline)) {
         if (kt < w0 || kt >= w1) return;
-        const float* ks = sK[buf];
-        const float* vs = sV[buf];
+        int lx = lane_xor, cl[T::kDB];
+#pragma unroll
+        for (int db = 0; db < T::kDB; ++db) cl[db] = col_lane[db];
+        opaque_lanes<T::kDB>(lx, cl);
         // S^T = K Q^T, dP^T = V dO^T (rows: the tile's keys, columns: the
         // wave's queries)
         floatx16 sacc = floatx16{}, pacc = floatx16{};
-        const float* krow = ks + l32 * T::kStr + h * T::kHalfD;
-        const float* vrow = vs + l32 * T::kStr + h * T::kHalfD;
 #pragma unroll
         for (int s = 0; s < T::kHalfD; s += 4) {
-            const floatx4 ka = *reinterpret_cast<const floatx4*>(krow + s);
-            const floatx4 va = *reinterpret_cast<const floatx4*>(vrow + s);
+            const floatx4 ka = f32_row_read<D>(ks, lane_row, lx, s);
+            const floatx4 va = f32_row_read<D>(vs, lane_row, lx, s);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[u], qf[s + u], sacc, 0, 0, 0);
@@ -1318,24 +1386,25 @@ fa2_bwd_dq_f32_kernel(const BwdParams p) {
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = acc_row(r, h);
 #pragma unroll
             for (int db = 0; db < T::kDB; ++db)
-                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[row * T::kStr + 32 * db + l32], pacc[r], dqacc[db], 0, 0, 0);
+                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(f32_col_read<D>(ks, cl, r, db), pacc[r], dqacc[db], 0, 0, 0);
         }
     };
 
-    if (n_kv > 0) {
-        ld.load(Kh, Vh, t0 * BN, N, tid);
-        ld.store(sK[0], sV[0], tid);
-    }
+    // ---- main loop, unrolled by two over the buffer pair (as in dK/dV)
+    if (n_kv > 0) issue(0, sK0, sV0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = 0; kt < n_kv; ++kt) {
-        const int buf = kt & 1;
-        const bool has_next = kt + 1 < n_kv;
-        if (has_next) ld.load(Kh, Vh, (t0 + kt + 1) * BN, N, tid);
-        compute_tile(kt, buf);
-        if (has_next) ld.store(sK[buf ^ 1], sV[buf ^ 1], tid);
+    for (int kt = 0; kt < n_kv; kt += 2) {
+        if (kt + 1 < n_kv) issue(kt + 1, sK1, sV1);
+        compute_tile(kt, sK0, sV0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 >= n_kv) break;
+        if (kt + 2 < n_kv) issue(kt + 2, sK0, sV0);
+        compute_tile(kt + 1, sK1, sV1);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
