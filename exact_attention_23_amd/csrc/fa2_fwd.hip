@@ -9,9 +9,11 @@
 //    ("Writing FlashAttention 2 in Triton", Step 1; "From FlashAttention to
 //    FlashAttention 2", section "2. Swapping the Loop Order");
 //  * the online-softmax recurrence with running max m, running sum l and an
-//    unnormalised O, all fp32, rescaled by exp(m_old - m_new) on each K/V tile
-//    ("FlashAttention-2 from PyTorch to Triton", the tile loop and the
+//    unnormalised O, all fp32, rescaled by exp(m_old - m_new) when the max
+//    moves ("FlashAttention-2 from PyTorch to Triton", the tile loop and the
 //    accumulator discussion; "Writing FlashAttention 2 in Triton", Step 4);
+//    the kernels move it only when the weights would otherwise leave the
+//    range their formats hold (see the kernels), which changes rounding only;
 //  * one division by l at the end ("Writing FlashAttention 2 in Triton",
 //    Step 5; "From FlashAttention to FlashAttention 2", section "1. Reducing
 //    Non-Matmul FLOPs");
@@ -38,10 +40,10 @@
 //    MFMA (lane = query, 8 keys per lane).  The A operand, V^T, is read from a
 //    row-major LDS copy of V with ds_read_b64_tr_b16 (bf16), or one key per
 //    lane with plain reads (fp32).
-//  * bf16: K and V tiles are copied global -> LDS by the load unit (buffer
-//    loads with the LDS bit, 16 bytes per lane) into XOR-swizzled rows and
-//    double-buffered; fp32: staged through VGPRs into padded rows.  Either
-//    way the next tile's loads are issued before the current tile's MFMAs.
+//  * K and V tiles are copied global -> LDS by the load unit (buffer loads
+//    with the LDS bit, 16 bytes per lane, no VGPR staging) into unpadded
+//    rows with XOR-swizzled 16-byte chunks, double-buffered; the next tile's
+//    copies are issued before the current tile's MFMAs.
 //  * Q stays in VGPRs for the whole K/V loop; O^T, m, l stay in registers.
 //  * Causal grids launch the heaviest query tiles first; batch*head is the
 //    fastest-varying grid index so that all tiles of one head land on the same
