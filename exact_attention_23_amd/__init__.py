@@ -238,12 +238,12 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    else:
+        _check_buffer(out, q.shape, q.dtype, q.device, "out")
     if lse is None:
         lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
-    elif lse.shape != (B, H, M) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor of shape [B,H,M]")
+    else:
+        _check_buffer(lse, (B, H, M), torch.float32, q.device, "lse")
     code = _dtype_code(q)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     wl, wr = int(window[0]), int(window[1])
@@ -272,6 +272,16 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if st != FA2_OK:
         raise Fa2Error(st)
     return out, lse
+
+
+def _check_buffer(t, shape, dtype, device, name):
+    """A caller-supplied output: the C entry points size their writes from the
+    problem's shape, so a buffer that is short, of another type, strided or on
+    another device is refused before any launch."""
+    import torch
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or not t.is_contiguous() or t.device != device):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {list(shape)} on {device}")
 
 
 def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
@@ -307,8 +317,12 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causa
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_buffer(out, q.shape, q.dtype, q.device, "out")
     if lse is None:
         lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    else:
+        _check_buffer(lse, (H, total_q), torch.float32, q.device, "lse")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
         st = fa2_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -355,15 +369,14 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     def _out(t, like, name):
         if t is None:
             return torch.empty_like(like)
-        if t.shape != like.shape or t.dtype != like.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like its input")
+        _check_buffer(t, like.shape, like.dtype, like.device, name)
         return t
 
     dq, dk, dv = _out(dq, q, "dq"), _out(dk, k, "dk"), _out(dv, v, "dv")
     if delta is None:
         delta = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
-    elif delta.shape != (B, H, M) or delta.dtype != torch.float32 or not delta.is_contiguous():
-        raise ValueError("delta must be a contiguous float32 tensor of shape [B,H,M]")
+    else:
+        _check_buffer(delta, (B, H, M), torch.float32, q.device, "delta")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
         st = fa2_bwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),

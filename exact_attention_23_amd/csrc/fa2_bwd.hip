@@ -1537,7 +1537,7 @@ int bwd_launch(const BwdEntry* e, BwdParams prm, int64_t rows, int64_t n_kt, int
         void* args[] = {&prm};
         err = hipLaunchKernel(e->dq, dim3((unsigned)(n_qt * prm.BH)), dim3(e->q_threads), args, 0, st);
     }
-    return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+    return launch_status(err);
 }
 
 }  // namespace
@@ -1567,9 +1567,11 @@ extern "C" int fa2_bwd_local(const void* q, const void* k, const void* v, const 
     if (!e) return FA2_ERR_UNSUPPORTED;
     // without a mask the query heads of a K/V head form one row sequence
     const KernelShape ks = kernel_shape(B, H, Hk, M, mask != kMaskNone);
-    // the 16-bit kernels copy one head's Q, dO (K, V) tiles through a buffer
-    // resource whose byte size is a 32-bit int
-    if (dtype != FA2_DTYPE_F32 && (ks.M * D * 2 >= kMax || N * D * 2 >= kMax)) return FA2_ERR_UNSUPPORTED;
+    // every backward kernel copies one head's Q, dO (K, V) tiles through a
+    // buffer resource whose byte size, and the tile offsets inside it, are
+    // 32-bit
+    const int64_t eb = dtype == FA2_DTYPE_F32 ? 4 : 2;
+    if (ks.M * D * eb >= kMax || N * D * eb >= kMax) return FA2_ERR_UNSUPPORTED;
     const int64_t n_kt = ceil_div(N, e->kv_block_n);
     const int64_t n_qt = ceil_div(ks.M, e->q_block_m);
     if (n_kt * BHk >= kMax || n_qt * ks.BH >= kMax) return FA2_ERR_UNSUPPORTED;
@@ -1626,8 +1628,8 @@ extern "C" int fa2_bwd_varlen(const void* q, const void* k, const void* v, const
     if (chk != FA2_OK) return chk;
 
     const int64_t kMax = (int64_t)1 << 31;
-    // row offsets inside a head are 32-bit (the 16-bit kernels: byte offsets)
-    const int64_t elt = dtype == FA2_DTYPE_F32 ? 1 : 2;
+    // byte offsets inside a head are 32-bit (buffer-resource tile copies)
+    const int64_t elt = dtype == FA2_DTYPE_F32 ? 4 : 2;
     if (B >= kMax || H >= kMax || Hk >= kMax || total_q * D * elt >= kMax || total_k * D * elt >= kMax ||
         H * total_q >= kMax)
         return FA2_ERR_UNSUPPORTED;

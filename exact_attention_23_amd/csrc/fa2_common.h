@@ -10,6 +10,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include "fa2.h"
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -170,6 +172,21 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Status of a kernel launch: the runtime finding no device, or no code object
+// for the current device (this library holds gfx950 code only), is
+// FA2_ERR_NO_DEVICE; any other refusal is FA2_ERR_LAUNCH.
+int launch_status(hipError_t e) {
+    switch (e) {
+        case hipSuccess: return FA2_OK;
+        case hipErrorNoDevice:
+        case hipErrorInvalidDevice:
+        case hipErrorNoBinaryForGpu:
+        case hipErrorInvalidDeviceFunction:
+        case hipErrorInsufficientDriver: return FA2_ERR_NO_DEVICE;
+        default: return FA2_ERR_LAUNCH;
+    }
+}
 
 // The problem as the kernels see it.  Without a causal mask, the G query
 // heads that share a K/V head are consecutive in q, o and lse, so their rows

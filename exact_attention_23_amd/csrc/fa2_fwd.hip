@@ -1425,14 +1425,14 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
     const KernelShape ks = kernel_shape(B, H, Hk, M, causal);
     if (ks.M * D >= kMax) return FA2_ERR_UNSUPPORTED;
     const Entry* e = find_entry(dtype, D, causal, ks.M);
-    // the 16-bit kernels address one head's K (V) through a buffer resource
-    // whose byte size is a 32-bit int
-    if (dtype != FA2_DTYPE_F32 && N * D * 2 >= kMax) return FA2_ERR_UNSUPPORTED;
+    // every forward kernel copies one head's K (V) tiles through a buffer
+    // resource whose byte size, and the tile offsets inside it, are 32-bit
+    const int64_t elt = dtype == FA2_DTYPE_F32 ? 4 : 2;
+    if (N * D * elt >= kMax || ks.M * D * elt >= kMax) return FA2_ERR_UNSUPPORTED;
     const int splits = n_splits == 0 ? choose_splits(*e, ks.BH, ks.M, N) : n_splits;
     const int64_t n_qt = ceil_div(ks.M, e->block_m);
     if (n_qt * ks.BH * splits >= kMax) return FA2_ERR_UNSUPPORTED;
 
-    const size_t elt = dtype == FA2_DTYPE_F32 ? 4 : 2;
     const size_t o_bytes = (size_t)BH * M * D * elt;
     const size_t kv_bytes = (size_t)B * Hk * N * D * elt;
     const size_t lse_bytes = (size_t)BH * M * 4;
@@ -1487,7 +1487,7 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
         void* margs[] = {(void*)&ws_o, (void*)&ws_l, &o, &lse, &rows, &ns};
         err = hipLaunchKernel(me->kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), margs, 0, st);
     }
-    return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+    return launch_status(err);
 }
 
 extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1545,7 +1545,7 @@ extern "C" int fa2_fwd_local(const void* q, const void* k, const void* v, void* 
     void* args[] = {&prm};
     const hipError_t err = hipLaunchKernel(e->kernel, dim3((unsigned)(n_qt * BH)), dim3(e->threads), args, 0,
                                            static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+    return launch_status(err);
 }
 
 extern "C" int fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1602,7 +1602,7 @@ extern "C" int fa2_fwd_varlen(const void* q, const void* k, const void* v, void*
     void* args[] = {&prm};
     const hipError_t err = hipLaunchKernel(e->kernel, dim3((unsigned)(n_qt * BH)), dim3(e->threads), args, 0,
                                            static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+    return launch_status(err);
 }
 
 extern "C" const char* fa2_status_string(int status) {

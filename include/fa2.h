@@ -43,7 +43,8 @@ typedef enum {
     FA2_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad scale */
     FA2_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement (e.g. D) */
     FA2_ERR_LAUNCH = 3,           /* the HIP runtime refused the launch */
-    FA2_ERR_NO_DEVICE = 4         /* no usable gfx950 device for the current context */
+    FA2_ERR_NO_DEVICE = 4         /* the runtime has no device, or none this build's gfx950
+                                     code runs on, for the launch */
 } fa2_status;
 
 /*
@@ -89,12 +90,20 @@ typedef enum {
  * pointer may be NULL only when its buffer holds no element (q, o, lse when
  * B*H*M == 0; k, v when B == 0).
  *
+ * Sizes: one head's q (o) and one head's k (v) must each stay under 2^31
+ * bytes (the kernels address a head through 32-bit byte offsets), i.e.
+ * M * D * elt < 2^31 and N * D * elt < 2^31 with elt = 4 for F32 and 2 for
+ * BF16 / F16; B * H and the grid must stay under 2^31 as well.  Larger
+ * problems are FA2_ERR_UNSUPPORTED, found before any launch.
+ *
  * Errors: all argument checks run before any HIP call; on failure nothing is
  * launched and the outputs are untouched.  M == 0 or B*H == 0 returns FA2_OK
  * without a launch.  On success one kernel is enqueued on `stream` and the
  * call returns without synchronising; faults inside the kernel surface at
- * the caller's next synchronisation.  FA2_ERR_LAUNCH is returned when the
- * runtime rejects the launch.
+ * the caller's next synchronisation.  When the runtime rejects the launch
+ * the call returns FA2_ERR_NO_DEVICE if it found no device, or no code object
+ * for the current one (the library holds gfx950 code only), and
+ * FA2_ERR_LAUNCH for any other refusal.
  */
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
@@ -251,7 +260,10 @@ int fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* 
  *
  * Arguments as for fa2_fwd_ex (B, H, Hk, M, N >= 1, D, scale, causal, dtype,
  * stream).  This build supports dtype F32, BF16 and F16 with D = 64 or 128
- * (F32: fp32 products throughout, P and dS included).
+ * (F32: fp32 products throughout, P and dS included).  Size limits as for
+ * fa2_fwd (per head of q, dout: M * D * elt < 2^31 bytes, taken over the
+ * H / Hk query heads of a K/V head together when there is no mask; per head
+ * of k, v: N * D * elt < 2^31).
  *
  * Ownership: every buffer is caller-allocated device memory; the library
  * allocates nothing.  The outputs dq, dk, dv and delta must not overlap each

@@ -92,3 +92,31 @@ def test_invalid_call_leaves_outputs_untouched():
     assert st == fa2.FA2_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert torch.all(o == 7.0) and torch.all(lse == 7.0)
+
+
+def test_wrong_output_buffers_refused_before_launch():
+    # caller-supplied outputs that are short, mistyped, strided or absent from
+    # the device raise before any launch, and the buffers keep their contents
+    q, k, v = (t.cuda() for t in workloads.make_inputs(1, 2, 64, 64, 64, "bf16", seed=5))
+    bad_outs = [torch.full((1, 2, 63, 64), 7.0, dtype=torch.bfloat16, device="cuda"),
+                torch.full((1, 2, 64, 64), 7.0, dtype=torch.float32, device="cuda"),
+                torch.full((1, 2, 64, 128), 7.0, dtype=torch.bfloat16, device="cuda")[..., :64],
+                torch.full((1, 2, 64, 64), 7.0, dtype=torch.bfloat16)]
+    for out in bad_outs:
+        with pytest.raises(ValueError):
+            fa2.forward(q, k, v, out=out)
+    for lse in (torch.full((1, 2, 63), 7.0, device="cuda"),
+                torch.full((1, 2, 64), 7.0, dtype=torch.float64, device="cuda")):
+        with pytest.raises(ValueError):
+            fa2.forward(q, k, v, lse=lse)
+    # packed sequences: [H, total, D] with two sequences of 40 and 24 rows
+    qp, kp, vp = (t.reshape(2, 64, 64).contiguous() for t in (q, k, v))
+    cu = torch.tensor([0, 40, 64], dtype=torch.int32, device="cuda")
+    short = torch.full((2, 60, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fa2.forward_varlen(qp, kp, vp, cu, cu, 40, out=short)
+    with pytest.raises(ValueError):
+        fa2.forward_varlen(qp, kp, vp, cu, cu, 40, lse=torch.full((2, 64), 7.0, dtype=torch.bfloat16,
+                                                                     device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(short == 7.0) and all(torch.all(o == 7.0) for o in bad_outs)
