@@ -5,7 +5,7 @@ kernels of ``libfa2.so``.  PyTorch is used for device memory and streams.
 There is no CPU fallback: if the library is missing, importing the binding
 raises.
 
-``fa2_fwd``, ``fa2_fwd_ex``, ``fa2_fwd_workspace_bytes``,
+``fa2_fwd``, ``fa2_fwd_ex``, ``fa2_fwd_ex_noalloc``, ``fa2_fwd_workspace_bytes``,
 ``fa2_fwd_num_splits``, ``fa2_fwd_local``, ``fa2_fwd_varlen``, ``fa2_bwd``,
 ``fa2_bwd_local`` and ``fa2_bwd_varlen`` mirror the C entry points of
 ``include/fa2.h`` one to one (raw device pointers and sizes).  ``forward``,
@@ -21,8 +21,8 @@ import math
 import os
 
 __all__ = ["FA2_DTYPE_F32", "FA2_DTYPE_BF16", "FA2_DTYPE_F16", "FA2_OK", "FA2_ERR_INVALID_ARGUMENT",
-           "FA2_ERR_UNSUPPORTED", "FA2_ERR_LAUNCH", "FA2_ERR_NO_DEVICE", "FA2_MAX_SPLITS", "Fa2Error",
-           "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_workspace_bytes", "fa2_fwd_num_splits", "fa2_fwd_local",
+           "FA2_ERR_UNSUPPORTED", "FA2_ERR_LAUNCH", "FA2_ERR_NO_DEVICE", "FA2_ERR_SCRATCH", "FA2_MAX_SPLITS",
+           "FA2_NOALLOC_SCRATCH_BYTES", "Fa2Error", "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_ex_noalloc", "fa2_fwd_workspace_bytes", "fa2_fwd_num_splits", "fa2_fwd_local",
            "fa2_fwd_varlen", "fa2_bwd", "fa2_bwd_local", "fa2_bwd_varlen", "fa2_status_string", "forward",
            "forward_varlen", "backward", "backward_varlen", "attention", "library_path", "EXPORTED_SYMBOLS"]
 
@@ -35,10 +35,13 @@ FA2_ERR_INVALID_ARGUMENT = 1
 FA2_ERR_UNSUPPORTED = 2
 FA2_ERR_LAUNCH = 3
 FA2_ERR_NO_DEVICE = 4
+FA2_ERR_SCRATCH = 5
 
 FA2_MAX_SPLITS = 128
+FA2_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
-EXPORTED_SYMBOLS = ("fa2_bwd", "fa2_bwd_local", "fa2_bwd_varlen", "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_local",
+EXPORTED_SYMBOLS = ("fa2_bwd", "fa2_bwd_local", "fa2_bwd_varlen", "fa2_fwd", "fa2_fwd_ex", "fa2_fwd_ex_noalloc",
+                    "fa2_fwd_local",
                     "fa2_fwd_num_splits", "fa2_fwd_varlen", "fa2_fwd_workspace_bytes", "fa2_status_string")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -66,7 +69,7 @@ def _hip_runtimes_mapped():
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is not built; run `python -m exact_attention_23_amd.build` "
+            f"{_LIB_PATH} is not built; run `python exact_attention_23_amd/build.py` "
             "(there is no fallback implementation)")
     # Device memory and streams come from torch, so libfa2 must bind to torch's
     # HIP runtime.  Importing torch first makes the loader resolve libfa2's
@@ -90,6 +93,12 @@ def _load():
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+    ]
+    lib.fa2_fwd_ex_noalloc.restype = ctypes.c_int
+    lib.fa2_fwd_ex_noalloc.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
     ]
     lib.fa2_fwd_workspace_bytes.restype = ctypes.c_int64
     lib.fa2_fwd_workspace_bytes.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
@@ -138,6 +147,15 @@ def fa2_fwd_ex(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Hk: int
     K/V); pointers are integers.  Returns the fa2_status code."""
     return int(_lib.fa2_fwd_ex(q, k, v, o, lse, B, H, Hk, M, N, D, scale, causal, dtype, n_splits,
                                workspace, workspace_size, stream))
+
+
+def fa2_fwd_ex_noalloc(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Hk: int, M: int, N: int,
+                       D: int, scale: float, causal: int, dtype: int, n_splits: int, stream: int | None) -> int:
+    """Direct call of the allocation-free C entry point (split partials in the
+    library's static device scratch array); pointers are integers.  Returns
+    the fa2_status code."""
+    return int(_lib.fa2_fwd_ex_noalloc(q, k, v, o, lse, B, H, Hk, M, N, D, scale, causal, dtype, n_splits,
+                                       stream))
 
 
 def fa2_fwd_workspace_bytes(B: int, H: int, M: int, D: int, n_splits: int) -> int:

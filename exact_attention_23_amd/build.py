@@ -1,6 +1,6 @@
 """Builds libfa2.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m exact_attention_23_amd.build [--resource-usage]
+    python exact_attention_23_amd/build.py [--resource-usage]
 """
 from __future__ import annotations
 

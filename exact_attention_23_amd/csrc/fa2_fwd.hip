@@ -59,6 +59,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "fa2.h"
 #include "fa2_common.h"
@@ -1396,10 +1398,45 @@ extern "C" int fa2_fwd_num_splits(int64_t B, int64_t H, int64_t Hk, int64_t M, i
     return choose_splits(*e, ks.BH, ks.M, N);
 }
 
-extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
-                          int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
-                          float scale, int causal, int dtype, int n_splits,
-                          void* workspace, int64_t workspace_size, void* stream) {
+// Split-K/V partials for callers that cannot allocate (fa2_fwd_ex_noalloc):
+// one array per device, kept until the process ends.  Its name is a host-side
+// stand-in; host code only ever uses the device address that
+// hipGetSymbolAddress returns for it (scratch_address).
+static __device__ __align__(256) char scratch[FA2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's `scratch` array, looked up once per
+// device (with that device current) and kept; FA2_OK or the failure status.
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return launch_status(err);
+    if (dev < 0 || dev >= kMaxDevices) return FA2_ERR_NO_DEVICE;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (err != hipSuccess || p == nullptr) return err != hipSuccess ? launch_status(err) : FA2_ERR_LAUNCH;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return FA2_OK;
+}
+
+// fa2_fwd_ex, with the split workspace either the caller's or (use_scratch)
+// the device's static scratch array.
+int fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+           float scale, int causal, int dtype, int n_splits,
+           void* workspace, int64_t workspace_size, bool use_scratch, void* stream) {
     // ---- argument checks, all before any HIP call
     if (B < 0 || H < 0 || Hk < 1 || M < 0 || N <= 0 || D <= 0) return FA2_ERR_INVALID_ARGUMENT;
     // a pointer may be null only when its buffer holds no element
@@ -1442,7 +1479,9 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
         overlaps(lse, lse_bytes, o, o_bytes))
         return FA2_ERR_INVALID_ARGUMENT;
     const int64_t ws_need = workspace_bytes(BH, M, D, splits);
-    if (ws_need > 0) {
+    if (use_scratch) {
+        if (ws_need > FA2_NOALLOC_SCRATCH_BYTES) return FA2_ERR_SCRATCH;
+    } else if (ws_need > 0) {
         if (!workspace || workspace_size < ws_need || misaligned(workspace, 16))
             return FA2_ERR_INVALID_ARGUMENT;
         const size_t w = (size_t)ws_need;
@@ -1453,6 +1492,10 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
     }
 
     if (M == 0 || BH == 0) return FA2_OK;
+    if (use_scratch && ws_need > 0) {
+        const int st = scratch_address(&workspace);
+        if (st != FA2_OK) return st;
+    }
 
     FwdParams prm{};  // dense layout, no window: cu_q = cu_k = null
     prm.q = q; prm.k = k; prm.v = v; prm.o = o; prm.lse = lse;
@@ -1488,6 +1531,23 @@ extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, 
         err = hipLaunchKernel(me->kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), margs, 0, st);
     }
     return launch_status(err);
+}
+
+}  // namespace
+
+extern "C" int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+                          float scale, int causal, int dtype, int n_splits,
+                          void* workspace, int64_t workspace_size, void* stream) {
+    return fwd_ex(q, k, v, o, lse, B, H, Hk, M, N, D, scale, causal, dtype, n_splits, workspace,
+                  workspace_size, false, stream);
+}
+
+extern "C" int fa2_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+                                  float scale, int causal, int dtype, int n_splits, void* stream) {
+    return fwd_ex(q, k, v, o, lse, B, H, Hk, M, N, D, scale, causal, dtype, n_splits, nullptr, 0, true,
+                  stream);
 }
 
 extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1612,6 +1672,7 @@ extern "C" const char* fa2_status_string(int status) {
         case FA2_ERR_UNSUPPORTED: return "FA2_ERR_UNSUPPORTED: head dimension or problem size not supported by this build";
         case FA2_ERR_LAUNCH: return "FA2_ERR_LAUNCH: the HIP runtime rejected the kernel launch";
         case FA2_ERR_NO_DEVICE: return "FA2_ERR_NO_DEVICE: no usable gfx950 device";
+        case FA2_ERR_SCRATCH: return "FA2_ERR_SCRATCH: the split partials need more than the static scratch array (FA2_NOALLOC_SCRATCH_BYTES) holds";
         default: return "unknown fa2 status";
     }
 }

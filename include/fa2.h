@@ -43,8 +43,10 @@ typedef enum {
     FA2_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad scale */
     FA2_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement (e.g. D) */
     FA2_ERR_LAUNCH = 3,           /* the HIP runtime refused the launch */
-    FA2_ERR_NO_DEVICE = 4         /* the runtime has no device, or none this build's gfx950
+    FA2_ERR_NO_DEVICE = 4,        /* the runtime has no device, or none this build's gfx950
                                      code runs on, for the launch */
+    FA2_ERR_SCRATCH = 5           /* fa2_fwd_ex_noalloc: the split partials would not fit
+                                     the static scratch array */
 } fa2_status;
 
 /*
@@ -75,7 +77,8 @@ typedef enum {
  *
  * Ownership: all buffers are allocated and owned by the caller on the
  * current HIP device; the library allocates nothing and keeps no state, so
- * concurrent calls on different streams are safe.  o must not overlap q, k or
+ * concurrent calls on different streams are safe (fa2_fwd_ex_noalloc, which
+ * shares one static array per device, is the exception).  o must not overlap q, k or
  * v, and lse must not overlap any other buffer.  Every entry point of this
  * header only enqueues kernels on `stream` (no allocation, no memset, no
  * synchronisation), so a call may be captured into a HIP graph and replayed;
@@ -151,6 +154,36 @@ int fa2_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
                float scale, int causal, int dtype, int n_splits,
                void* workspace, int64_t workspace_size, void* stream);
+
+/* Bytes of the static device scratch array behind fa2_fwd_ex_noalloc. */
+#define FA2_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+
+/*
+ * fa2_fwd_ex_noalloc -- fa2_fwd_ex for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the split-K/V partials go to a static device array of
+ * FA2_NOALLOC_SCRATCH_BYTES bytes that the library holds on every device it
+ * runs on until the process ends, instead of a caller workspace.
+ *
+ * Arguments, layout, results and errors as for fa2_fwd_ex without the
+ * workspace arguments; the output is bitwise the same as fa2_fwd_ex's with
+ * the same effective split count.  A problem whose partials need more than
+ * the array holds (fa2_fwd_workspace_bytes(B, H, M, D, splits) >
+ * FA2_NOALLOC_SCRATCH_BYTES) returns FA2_ERR_SCRATCH before any HIP call;
+ * pass a smaller n_splits (1 needs no scratch) or use fa2_fwd_ex.
+ *
+ * The call allocates nothing: it enqueues the same kernels as fa2_fwd_ex.
+ * On its first call on a device (with that device current) it looks up the
+ * array's device address with hipGetSymbolAddress and keeps it.  Nothing in
+ * the array needs to start at zero (every partial a launch reads was written
+ * by the same launch), but all calls on one device share the one array:
+ * calls whose kernels overlap in time on one device (concurrent streams, or
+ * host threads) race on it and give undefined results.  Serialise them, or
+ * use fa2_fwd_ex with a workspace per stream.
+ */
+int fa2_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
+                       float scale, int causal, int dtype, int n_splits, void* stream);
 
 /*
  * fa2_fwd_workspace_bytes -- workspace fa2_fwd_ex needs for n_splits splits

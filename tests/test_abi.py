@@ -230,6 +230,37 @@ def test_f32_head_addressed_by_32bit_buffer_size(D, N):
     assert call_bwd_varlen(total_q=N, D=D, dtype=f32) == fa2.FA2_ERR_UNSUPPORTED
 
 
+def call_noalloc(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, Hk=1, M=16, N=16, D=64, scale=0.125, causal=0,
+                 dtype=fa2.FA2_DTYPE_BF16, n_splits=1):
+    return fa2.fa2_fwd_ex_noalloc(q, k, v, o, lse, B, H, Hk, M, N, D, scale, causal, dtype, n_splits, None)
+
+
+def test_noalloc_checks_match_fa2_fwd_ex():
+    # the allocation-free entry point runs fa2_fwd_ex's argument checks
+    for kw in (dict(q=0), dict(B=-1), dict(N=0), dict(H=4, Hk=3), dict(scale=0.0), dict(causal=2),
+               dict(dtype=9), dict(n_splits=-1), dict(n_splits=fa2.FA2_MAX_SPLITS + 1), dict(o=Q),
+               dict(k=K + 8)):
+        assert call_noalloc(**kw) == fa2.FA2_ERR_INVALID_ARGUMENT, kw
+    assert call_noalloc(D=96) == fa2.FA2_ERR_UNSUPPORTED
+    assert call_noalloc(M=0, n_splits=8) == fa2.FA2_OK
+
+
+def test_noalloc_refuses_partials_beyond_its_scratch():
+    # partials of 8 splits x 64 heads x 4096 rows x 128 fp32 = 1 GiB: refused
+    # before any HIP call; the same problem unsplit needs no scratch
+    G = 1 << 32  # fake buffers far enough apart not to overlap at this size
+    big = dict(q=G, k=2 * G, v=3 * G, o=4 * G, lse=5 * G, B=1, H=64, Hk=64, M=4096, N=4096, D=128, n_splits=8)
+    need = fa2.fa2_fwd_workspace_bytes(1, 64, 4096, 128, 8)
+    assert need > fa2.FA2_NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(**big) == fa2.FA2_ERR_SCRATCH
+    assert "scratch" in fa2.fa2_status_string(fa2.FA2_ERR_SCRATCH)
+    # the largest split count whose partials fit is accepted by the checks
+    fits = max(s for s in range(2, fa2.FA2_MAX_SPLITS + 1)
+               if fa2.fa2_fwd_workspace_bytes(1, 8, 64, 128, s) <= fa2.FA2_NOALLOC_SCRATCH_BYTES)
+    assert fits == fa2.FA2_MAX_SPLITS or fa2.fa2_fwd_workspace_bytes(1, 8, 64, 128, fits + 1) > \
+        fa2.FA2_NOALLOC_SCRATCH_BYTES
+
+
 @no_device_only
 def test_no_device_status():
     # a call that passes every check, in a process whose HIP runtime finds no
@@ -238,6 +269,11 @@ def test_no_device_status():
         assert call(dtype=dtype) == fa2.FA2_ERR_NO_DEVICE
         assert call_bwd(dtype=dtype) == fa2.FA2_ERR_NO_DEVICE
     assert call_local() == fa2.FA2_ERR_NO_DEVICE
+    # the allocation-free entry point, unsplit and split (its scratch lookup)
+    assert call_noalloc() == fa2.FA2_ERR_NO_DEVICE
+    G = 1 << 32
+    assert call_noalloc(q=G, k=2 * G, v=3 * G, o=4 * G, lse=5 * G, M=4, N=4096, D=128,
+                        n_splits=4) == fa2.FA2_ERR_NO_DEVICE
 
 
 # ------------------------------------------------------ fa2_bwd (no launches)
