@@ -85,8 +85,8 @@ def load_traffic(workload: str):
 
 def dominant_kernel(w, splits: int = 1) -> str:
     """The forward kernel the library launches for this workload (its
-    dispatch table: fp32 kernel, or the 16-bit kernel, ping-pong at D=128
-    on the dense unwindowed path unless a head has at most 64 rows),
+    dispatch table: fp32 kernel, or the 16-bit kernel, ping-pong on the
+    dense unwindowed path unless a head has at most 64 rows),
     followed by the combine kernel when the key range is split."""
     # rows per head of the kernel view: the grouped query heads of a K/V head
     # form one row sequence when there is no mask
@@ -96,7 +96,7 @@ def dominant_kernel(w, splits: int = 1) -> str:
     elif w.lengths is not None or w.window != (-1, -1) or rows <= 64:
         k = "fa2_fwd_half_kernel"
     else:
-        k = "fa2_fwd_half_pp_kernel" if w.D == 128 else "fa2_fwd_half_kernel"
+        k = "fa2_fwd_half_pp_kernel"
     return k + (f" x{splits} splits + fa2_merge_kernel" if splits > 1 else "")
 
 

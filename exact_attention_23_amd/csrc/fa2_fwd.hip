@@ -48,9 +48,9 @@
 //  * Causal grids launch the heaviest query tiles first; batch*head is the
 //    fastest-varying grid index so that all tiles of one head land on the same
 //    XCD (workgroups are dealt to the 8 XCDs round-robin).
-//  * bf16 at D = 128 uses a ping-pong schedule between two groups of four
-//    waves (see fa2_fwd_half_pp_kernel), because a wave's own MFMA and VALU
-//    work does not overlap on gfx950 while two waves on one SIMD do.
+//  * the dense 16-bit path uses a ping-pong schedule between two groups of
+//    four waves (see fa2_fwd_half_pp_kernel): one wave of a SIMD runs MFMAs
+//    while the other runs the softmax.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -591,10 +591,11 @@ fa2_fwd_half_kernel(const FwdParams p) {
 // ---------------------------------------------------------------------------
 // 16-bit kernel, ping-pong schedule
 // ---------------------------------------------------------------------------
-// On gfx950 a wave's own MFMA and VALU instructions do not overlap, but the
-// MFMA of one wave and the VALU of another wave on the same SIMD do.  This
-// kernel therefore runs two groups of four waves (waves w and w + 4 share a
-// SIMD) half a tile out of phase, separated by workgroup barriers:
+// A wave issues in order, so its softmax overlaps its own MFMAs only when
+// the two are interleaved instruction by instruction; the MFMA of one wave
+// and the VALU of another wave on the same SIMD overlap without that.  This
+// kernel runs two groups of four waves (waves w and w + 4 share a SIMD) half
+// a tile out of phase, separated by workgroup barriers:
 //
 //   period:     0        1        2          3          4 ...
 //   group A:  S(0)     sm(0)    PV(0)+S(1)  sm(1)      PV(1)+S(2)
@@ -1260,14 +1261,16 @@ struct Entry {
 #define FWD_KERNEL(...) reinterpret_cast<const void*>(&__VA_ARGS__)
 #define FWD_PAIR(name, ...) FWD_KERNEL(name<__VA_ARGS__, false>), FWD_KERNEL(name<__VA_ARGS__, true>)
 const Entry kTable[] = {
-    // bf16, fp16: 8 waves (two per SIMD) share each K/V tile; 256 query rows per
-    // workgroup; 64-key tiles at D=128, 128-key tiles at D=64 (measured best)
-    {FA2_DTYPE_BF16, 64, 0, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 64, 128, 8, 1, 2, kMaskNone), 512, 256, 128, 1},
-    {FA2_DTYPE_BF16, 64, 1, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 64, 128, 8, 1, 2, kMaskCausal), 512, 256, 128, 1},
+    // bf16, fp16: the ping-pong kernel, 8 waves (two per SIMD) sharing each
+    // 64-key K/V tile, 256 query rows per workgroup.  At D = 64 it measured 5 %
+    // faster than the plain 8-wave kernel (128-key tiles) on the ragged
+    // cross-attention workload; 128-key ping-pong tiles gained nothing there.
+    {FA2_DTYPE_BF16, 64, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 64, 64, false), 512, 256, 64, 1},
+    {FA2_DTYPE_BF16, 64, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 64, 64, true), 512, 256, 64, 1},
     {FA2_DTYPE_BF16, 128, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 128, 64, false), 512, 256, 64, 1},
     {FA2_DTYPE_BF16, 128, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 128, 64, true), 512, 256, 64, 1},
-    {FA2_DTYPE_F16, 64, 0, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 64, 128, 8, 1, 2, kMaskNone), 512, 256, 128, 1},
-    {FA2_DTYPE_F16, 64, 1, FWD_PAIR(fa2_fwd_half_kernel, _Float16, 64, 128, 8, 1, 2, kMaskCausal), 512, 256, 128, 1},
+    {FA2_DTYPE_F16, 64, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 64, 64, false), 512, 256, 64, 1},
+    {FA2_DTYPE_F16, 64, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 64, 64, true), 512, 256, 64, 1},
     {FA2_DTYPE_F16, 128, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, false), 512, 256, 64, 1},
     {FA2_DTYPE_F16, 128, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, true), 512, 256, 64, 1},
     // fp32: 4 waves, 128 query rows; at D = 64 non-causal 32-key tiles with
@@ -1342,8 +1345,8 @@ int choose_splits(const Entry& e, int64_t BH, int64_t M, int64_t N) {
 }
 
 // Sliding-window and packed-sequence entry points: the general 8-wave 16-bit
-// kernel (also at D = 128, where the dense entry point uses the ping-pong
-// kernel) and the fp32 kernel, one instantiation per mask kind, unsplit.
+// kernel (the dense entry point uses the ping-pong kernel instead) and the
+// fp32 kernel, one instantiation per mask kind, unsplit.
 struct LocalEntry {
     int dtype, D, mask;
     const void* kernel;
