@@ -15,7 +15,12 @@ non-causal).  Prints ONE JSON line with the whole-job throughput
   against MI355X's dense MFMA peak for the dtype; traffic = HBM bytes per
   launch from the committed rocprofv3 counter summary, when it was taken on
   the current kernel source;
-* cpu_baseline: the CPU oracle timed on this host on the same workload;
+* sclk: the shader clock the driver reports while the timed steps run;
+* cpu_baseline: the CPU oracle timed on this host on the same workload
+  (value), and on each of the five configurations with the max-abs error of
+  the GPU's O and L against it (configs; the long-context one on its sample
+  of query rows, with the full run extrapolated and labelled as such), plus
+  the tiny configuration on a single core;
 * workloads: per-launch latency (median of 100 after 25 warm-ups, with and
   without an L2/MALL flush before each launch) of every workload;
 * backward: per-call latency of fa2_bwd (delta, dK/dV and dQ kernels) on the
@@ -151,21 +156,141 @@ def median(xs):
     return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
 
 
-def cpu_baseline(w):
-    """The fp64 oracle, as it stands, on the whole workload (one pass)."""
+# parity tolerances of the comparison with the oracle (max-abs on O, on L)
+TOLERANCE = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-3), "f16": (5e-3, 1e-3)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _f32_carrier(t):
+    """The exact float32 values of an input tensor (bf16 / fp16 widened)."""
+    import torch
+    return t.to(torch.float32).contiguous().numpy()
+
+
+def _sampled_flops(w, rows) -> float:
+    """Counted work of the listed query rows: 4*D flop per visible (query,
+    key) pair, over every head."""
+    if rows is None:
+        return w.flops
+    pairs = sum(min(int(i) + 1, w.N) if w.causal else w.N for i in rows)
+    return 4.0 * w.B * w.H * w.D * pairs
+
+
+def cpu_baseline(headline, gpu_forward):
+    """The fp64 oracle, as it stands, on this host: every workload of the
+    five configurations (all threads; config 4 on its seeded sample of query
+    rows, with the full run extrapolated by visible pairs and labelled as
+    such), the tiny configuration once more on one core, and the max-abs
+    error of the GPU result against it per configuration.  `gpu_forward(w, q,
+    k, v)` returns the GPU's (o, lse) as float64 arrays."""
+    import numpy as np
     import oracle
     import workloads
-    q, k, v = workloads.workload_inputs(w)
-    rows = workloads.sample_rows(w)
     threads = oracle.max_threads()
+    configs = []
+    head = None
+    for name in workloads.ORDER:
+        w = workloads.get(name)
+        q, k, v = workloads.workload_inputs(w)
+        rows = workloads.sample_rows(w)
+        rows_np = None if rows is None else rows.numpy()
+        qa, ka, va = _f32_carrier(q), _f32_carrier(k), _f32_carrier(v)
+        t0 = time.perf_counter()
+        o_ref, l_ref = oracle.attention(qa, ka, va, w.scale, w.causal, rows=rows_np)
+        dt = time.perf_counter() - t0
+        del qa, ka, va
+        o_gpu, l_gpu = gpu_forward(w, q, k, v)
+        if rows_np is not None:
+            o_gpu, l_gpu = o_gpu[:, :, rows_np], l_gpu[:, :, rows_np]
+        err_o = float(np.abs(o_gpu - o_ref).max())
+        err_l = float(np.abs(l_gpu - l_ref).max())
+        tol_o, tol_l = TOLERANCE[w.dtype]
+        flops = _sampled_flops(w, rows_np)
+        entry = {"workload": w.name, "rows_checked": "all" if rows_np is None else
+                 f"{len(rows_np)} per head (seeded sample, rows 0 and M-1 included)",
+                 "oracle_s": round(dt, 3), "oracle_tflops": round(flops / dt / 1e12, 4), "cores": threads,
+                 "max_abs_o": err_o, "max_abs_l": err_l, "tolerance_o": tol_o, "tolerance_l": tol_l,
+                 "within_tolerance": bool(err_o <= tol_o and err_l <= tol_l)}
+        if rows_np is not None:
+            entry["oracle_s_full_extrapolated"] = round(dt * w.flops / flops, 1)
+            entry["extrapolation"] = "measured time x (visible pairs of every row / of the sampled rows)"
+        configs.append(entry)
+        if w.name == headline.name:
+            head = (flops / dt / 1e12, dt, rows_np)
+        del q, k, v, o_ref, l_ref, o_gpu, l_gpu
+    # the tiny configuration on one core
+    w1 = workloads.get(workloads.ORDER[0])
+    q, k, v = (_f32_carrier(t) for t in workloads.workload_inputs(w1))
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, w.scale, w.causal, rows=None if rows is None else rows.numpy())
-    dt = time.perf_counter() - t0
-    flops = w.flops if rows is None else w.flops * len(rows) / w.M  # approximate for sampled rows
-    sample = (f"all {w.B}x{w.H}x{w.M} query rows of {w.name}, one pass" if rows is None else
-              f"{len(rows)} sampled rows per head of {w.name}")
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": dt}
+    oracle.attention(q, k, v, w1.scale, w1.causal, threads=1)
+    single = time.perf_counter() - t0
+    value, seconds, rows_np = head
+    sample = (f"all {headline.B}x{headline.H}x{headline.M} query rows of {headline.name}, one pass"
+              if rows_np is None else f"{len(rows_np)} sampled rows per head of {headline.name}")
+    return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "sample": sample,
+            "seconds": seconds, "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_core": {"workload": w1.name, "seconds": round(single, 4),
+                            "tflops": round(w1.flops / single / 1e12, 5), "cores": 1},
+            "configs": configs}
+
+
+class SclkSampler:
+    """Shader clock while the GPU works: the current-clock line of the amdgpu
+    driver's pp_dpm_sclk table, read every few milliseconds by a thread;
+    None where the file is not readable."""
+    PATHS = ("/sys/class/drm/card0/device/pp_dpm_sclk",)
+
+    def __init__(self, period_s: float = 0.002):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self.path = next((p for p in self.PATHS if os.access(p, os.R_OK)), None)
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    mhz = line.split(":", 1)[1].strip().rstrip("*").strip()
+                    return float(mhz.lower().replace("mhz", ""))
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                x = self._read()
+            except (OSError, ValueError):
+                x = None
+            if x is not None:
+                self.samples.append(x)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path is not None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path is not None:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"median_mhz": median(self.samples), "min_mhz": min(self.samples), "max_mhz": max(self.samples),
+                "samples": len(self.samples), "source": self.path}
 
 
 COPY_BYTES = 256 * 1024 * 1024
@@ -363,16 +488,17 @@ def main(argv=None):
         fn()
     torch.cuda.synchronize()
     events = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record(stream)
-        fn()
-        e.record(stream)
-        events.append((s, e))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with SclkSampler() as sclk:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fn()
+            e.record(stream)
+            events.append((s, e))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     launch_ms = [s.elapsed_time(e) for s, e in events]
     ms_per_step = wall * 1e3 / args.steps
     mean_launch_ms = sum(launch_ms) / len(launch_ms)
@@ -409,6 +535,7 @@ def main(argv=None):
                    "pass": args.which,
                    "global_batch": w.B, "seq_len": w.M, "parallelism": "single GPU"},
         "roofline": roofline,
+        "sclk": sclk.summary(),
     }
     del bufs
 
@@ -420,7 +547,8 @@ def main(argv=None):
             wx = workloads.get(name)
             bx = setup(wx)
             fx = launcher(wx, bx)
-            hot = time_launches(fx, stream, 25, 100, prewarm_s=args.prewarm)
+            with SclkSampler() as sc:
+                hot = time_launches(fx, stream, 25, 100, prewarm_s=args.prewarm)
             cold = time_launches(fx, stream, 3, 20, flush=flush_buf.zero_)
             us, us_cold = median(hot) * 1e3, median(cold) * 1e3
             tf = wx.flops / (us * 1e-6) / 1e12
@@ -435,7 +563,8 @@ def main(argv=None):
                            "us_median": round(us, 2), "us_median_l2_flushed": round(us_cold, 2),
                            "tflops": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK_TFLOPS[wx.dtype], 4),
                            "hbm_gbs_compulsory": round(wx.compulsory_bytes / (us * 1e-6) / 1e9, 1),
-                           "bound": bound, "frac_of_bound": round(ach / pk, 4)}
+                           "bound": bound, "frac_of_bound": round(ach / pk, 4),
+                           "sclk_mhz_median": (sc.summary() or {}).get("median_mhz")}
             del bx, fx
         result["workloads"] = table
         # backward passes (one fa2_bwd call each: delta, dK/dV, dQ kernels)
@@ -457,7 +586,13 @@ def main(argv=None):
         result["backward"] = btable
 
     if not args.no_cpu and not backward:
-        result["cpu_baseline"] = cpu_baseline(w)
+        import numpy as np
+
+        def gpu_forward(wx, q, k, v):
+            o, lse = fa2.forward(q.to(dev), k.to(dev), v.to(dev), causal=wx.causal)
+            torch.cuda.synchronize()
+            return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+        result["cpu_baseline"] = cpu_baseline(w, gpu_forward)
 
     print(json.dumps(result), flush=True)
     return 0
