@@ -904,17 +904,21 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
         lds_barrier();
     }
 
-    // ---- epilogue: one normalisation, L = (m + log2 l) * ln 2, RNE store
+    // ---- epilogue: one normalisation, L = (m + log2 l) * ln 2, RNE store.
+    // The rounded O goes through LDS (the wave's own 32 rows in a K/V buffer
+    // the loop no longer reads) so that it leaves as whole rows, 16 bytes per
+    // lane: a lane holds 4-value pieces of one row, and storing those
+    // directly would touch 32 rows per instruction.
     {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
         const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         const auto se = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_exact), __float_as_uint(l_exact), false, false);
         const float l_ex = __uint_as_float(se[0]) + __uint_as_float(se[1]);
         const int query = qw0 + l32;
-        if (query < M) {
-            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            const float lse = (m_run + fast_log2(l_ex)) * kLn2;
-            if constexpr (SPLIT) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float lse = (m_run + fast_log2(l_ex)) * kLn2;
+        if constexpr (SPLIT) {
+            if (query < M) {
                 float* orow = partial_row(p, task, query, D);
 #pragma unroll
                 for (int db = 0; db < T::kDB; ++db)
@@ -925,19 +929,34 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
                         *reinterpret_cast<floatx4*>(orow + 32 * db + 8 * g + 4 * h) = x;
                     }
                 if (h == 0) *partial_l(p, task, query) = lse;
-            } else {
-                E* orow = O + ((int64_t)bh * M + query) * D;
-#pragma unroll
-                for (int db = 0; db < T::kDB; ++db)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int d = 32 * db + 8 * g + 4 * h;
-                        const uint32_t w0 = pack2<E>(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-                        const uint32_t w1 = pack2<E>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-                        *reinterpret_cast<uint2*>(orow + d) = make_uint2(w0, w1);
-                    }
-                if (h == 0) LSE[(int64_t)bh * M + query] = lse;
             }
+        } else {
+            // the wave's 32 rows x D, rows of kRowBytes whose 16-byte chunks
+            // are XOR-swizzled by the row (conflict-free row reads, at most
+            // two-way conflicts on the 8-byte writes)
+            static_assert(32 * T::kRowBytes * 2 <= T::kTileBytes, "staging space");
+            char* stage = (wave < 2 ? sK0 : wave < 4 ? sV0 : wave < 6 ? sK1 : sV1) + (wave & 1) * 32 * T::kRowBytes;
+            const int rsw = l32 % T::kCPR;
+#pragma unroll
+            for (int db = 0; db < T::kDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c = 4 * db + g;  // 16-byte chunk (8 values of d) of the row
+                    const uint32_t w0 = pack2<E>(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+                    const uint32_t w1 = pack2<E>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+                    *reinterpret_cast<uint2*>(stage + l32 * T::kRowBytes + 16 * (c ^ rsw) + 8 * h) = make_uint2(w0, w1);
+                }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave reads back its own writes
+            constexpr int kRowsPerRead = 64 / T::kCPR;
+            const int rr = lane / T::kCPR, cc = lane % T::kCPR;
+            E* const obase = O + ((int64_t)bh * M + qw0) * D;
+#pragma unroll
+            for (int i = 0; i < 32 / kRowsPerRead; ++i) {
+                const int r = i * kRowsPerRead + rr;
+                const uint4 x = *reinterpret_cast<const uint4*>(stage + r * T::kRowBytes + 16 * (cc ^ (r % T::kCPR)));
+                if (qw0 + r < M) *reinterpret_cast<uint4*>(obase + (int64_t)r * D + 8 * cc) = x;
+            }
+            if (h == 0 && query < M) LSE[(int64_t)bh * M + query] = lse;
         }
     }
 }
