@@ -565,6 +565,11 @@ def main(argv=None):
                            "hbm_gbs_compulsory": round(wx.compulsory_bytes / (us * 1e-6) / 1e9, 1),
                            "bound": bound, "frac_of_bound": round(ach / pk, 4),
                            "sclk_mhz_median": (sc.summary() or {}).get("median_mhz")}
+            # the dtype's dense peak scaled to the clock the launches ran at
+            # (AMD's peak figures assume 2.4 GHz)
+            mhz = table[name]["sclk_mhz_median"]
+            table[name]["frac_of_mfma_peak_at_sclk"] = (
+                round(tf / (PEAK_TFLOPS[wx.dtype] * mhz / 2400.0), 4) if mhz else None)
             del bx, fx
         result["workloads"] = table
         # backward passes (one fa2_bwd call each: delta, dK/dV, dQ kernels)

@@ -76,6 +76,7 @@ static void report(const char* what, double err, double bound) {
 /* One forward case: fp32 inputs (rounded to bf16 first when bf16). */
 static void forward_case(const char* what, int dtype, int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N,
                          int64_t D, int causal, int n_splits) {
+    fprintf(stderr, "case %s\n", what);
     const size_t nq = (size_t)(B * H * M * D), nk = (size_t)(B * Hk * N * D), nl = (size_t)(B * H * M);
     float* q = malloc(nq * 4);
     float* k = malloc(nk * 4);
@@ -150,6 +151,7 @@ static void forward_case(const char* what, int dtype, int64_t B, int64_t H, int6
 /* fp32 forward then backward, gradients against the oracle's chain rule. */
 static void backward_case(const char* what, int64_t B, int64_t H, int64_t Hk, int64_t M, int64_t N, int64_t D,
                           int causal) {
+    fprintf(stderr, "case %s\n", what);
     const size_t nq = (size_t)(B * H * M * D), nk = (size_t)(B * Hk * N * D), nl = (size_t)(B * H * M);
     float* q = malloc(nq * 4);
     float* k = malloc(nk * 4);
@@ -207,6 +209,8 @@ static void backward_case(const char* what, int64_t B, int64_t H, int64_t Hk, in
 }
 
 int main(void) {
+    /* line-buffered: whatever was printed survives an abnormal end */
+    setvbuf(stdout, NULL, _IOLBF, 0);
     int n = 0;
     if (hipGetDeviceCount(&n) != hipSuccess || n < 1) {
         fprintf(stderr, "no HIP device\n");
