@@ -806,7 +806,21 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
     // weights stay negligible.  P is rounded once; l_exact sums the fp32
     // weights (for L), l_run the rounded ones (in the MFMA phase that
     // consumes P).
+    // (in three fenced groups: all exponents, all exponentials, then the
+    // rounding and the sums, so no consumer issues right behind the
+    // transcendental it waits for)
     auto weights = [&](float m_sub) {
+        float w[T::kKB][16];
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w[kb][r] = fmaf(sacc[kb][r], c_log2, -m_sub);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w[kb][r] = fast_exp2(w[kb][r]);
+        __builtin_amdgcn_sched_barrier(0);
         float esum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < T::kKB; ++kb)
@@ -814,12 +828,12 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
             for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
                 for (int u = 0; u < 8; u += 2) {
-                    const float p0 = fast_exp2(fmaf(sacc[kb][8 * ms + u], c_log2, -m_sub));
-                    const float p1 = fast_exp2(fmaf(sacc[kb][8 * ms + u + 1], c_log2, -m_sub));
+                    const float p0 = w[kb][8 * ms + u], p1 = w[kb][8 * ms + u + 1];
                     const V2 pp = {(E)p0, (E)p1};
                     pf[kb][ms][u] = pp[0];
                     pf[kb][ms][u + 1] = pp[1];
-                    esum[(u >> 1) & 3] += p0 + p1;
+                    esum[(u >> 1) & 3] += p0;
+                    esum[((u >> 1) + 1) & 3] += p1;
                 }
         return (esum[0] + esum[1]) + (esum[2] + esum[3]);
     };
