@@ -505,14 +505,18 @@ def main(argv=None):
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     if backward:
-        # one fa2_bwd call: delta, dK/dV and dQ kernels on one stream
+        # one fa2_bwd call on one stream: 16-bit dQ (with Delta) then dK/dV;
+        # fp32 Delta, dK/dV, dQ
         peak = PEAK_TFLOPS[w.dtype]
         achieved = step_flops / (mean_launch_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4), "traffic": None,
                     "mean_launch_us": round(mean_launch_ms * 1e3, 2),
-                    "kernel": f"fa2_bwd: fa2_bwd_delta_kernel + fa2_bwd_dkdv_kernel + fa2_bwd_dq_kernel "
-                              f"(D={w.D}, causal={int(w.causal)})"}
+                    "kernel": ("fa2_bwd: fa2_bwd_delta_f32_kernel + fa2_bwd_dkdv_f32_kernel + fa2_bwd_dq_f32_kernel"
+                               if w.dtype == "f32" else
+                               "fa2_bwd: fa2_bwd_dq_kernel (with Delta) + "
+                               + ("fa2_bwd_dkdv_pair_kernel" if w.D == 128 else "fa2_bwd_dkdv_kernel"))
+                              + f" (D={w.D}, causal={int(w.causal)})"}
         splits = 1
     else:
         bound, achieved, peak, unit = roofline_of(w, mean_launch_ms * 1e-3)

@@ -22,8 +22,10 @@
 // forward, stored for the backward).
 //
 // Schedule (our own design for gfx950):
-//  * a small kernel computes Delta per query row (HBM-bound, one pass over
-//    O and dO);
+//  * Delta per query row: the 16-bit dQ kernel computes it from the dO
+//    fragments it holds anyway and one read of O, and stores it for the
+//    dK/dV kernel, which runs after it; fp32 inputs use a small HBM-bound
+//    kernel (one pass over O and dO) ahead of the other two;
 //  * the dK/dV kernel gives each workgroup one tile of keys (32 per wave) of
 //    one K/V head and streams the query tiles of every query head of its
 //    group through LDS; K and V of the wave's keys stay in VGPRs (at
@@ -67,8 +69,9 @@ struct BwdParams {
     const void* k;
     const void* v;
     const void* dout;
+    const void* o;      // the forward's output (16-bit paths: read by the dQ kernel for Delta)
     const float* lse;
-    const float* delta;
+    float* delta;       // written by the Delta pass, read by the dK/dV kernel
     void* dq;
     void* dk;
     void* dv;
@@ -228,31 +231,6 @@ __device__ __forceinline__ void copy_offsets(uint32_t* off, int wave, int lane) 
         const int r = slot / kCPR, c = slot % kCPR;
         off[i] = (uint32_t)(r * 2 * D + 16 * (c ^ swz_rt<D>(r)));
     }
-}
-
-// ---------------------------------------------------------------------------
-// Delta = rowsum(dO o O), fp32
-// ---------------------------------------------------------------------------
-// D / 8 lanes per row, 16 bytes of O and dO each, reduced across the lanes.
-template <typename E, int D>
-__global__ void __launch_bounds__(256)
-fa2_bwd_delta_kernel(const E* __restrict__ O, const E* __restrict__ dO, float* __restrict__ delta, int rows) {
-    using V8 = typename Half<E>::v8;
-    constexpr int kLanes = D / 8;
-    constexpr int kRowsPerWave = 64 / kLanes;
-    const int lane = threadIdx.x & 63;
-    const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave + lane / kLanes;
-    const int c = lane % kLanes;
-    float acc = 0.f;
-    if (row < rows) {
-        const V8 a = *reinterpret_cast<const V8*>(O + (int64_t)row * D + 8 * c);
-        const V8 b = *reinterpret_cast<const V8*>(dO + (int64_t)row * D + 8 * c);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc = fmaf((float)a[i], (float)b[i], acc);
-    }
-#pragma unroll
-    for (int off = kLanes / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (row < rows && c == 0) delta[row] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -816,7 +794,28 @@ fa2_bwd_dq_kernel(const BwdParams p) {
         }
     }
     const float l2 = l2_of(query < M ? p.lse[qr + query] : INFINITY);
-    const float dl = query < M ? p.delta[qr + query] : 0.f;
+    // Delta = rowsum(dO o O) of the row (fp32 sums of the 16-bit products):
+    // each lane half holds half of the row's dO; the matching O values are
+    // read once, and the two halves' sums are exchanged.  Stored for the
+    // dK/dV kernel (0 past M, not stored).
+    float dl;
+    {
+        using V2 = typename Half<E>::v2;
+        const E* Oh = static_cast<const E*>(p.o) + qr * D;
+        float part = 0.f;
+        if (query < M) {
+#pragma unroll
+            for (int s = 0; s < T::kDS; ++s) {
+                const V8 ov = *reinterpret_cast<const V8*>(Oh + (int64_t)query * D + 16 * s + 8 * h);
+#pragma unroll
+                for (int j = 0; j < 8; j += 2)
+                    part = Half<E>::dot2(V2{of[s][j], of[s][j + 1]}, V2{ov[j], ov[j + 1]}, part);
+            }
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        dl = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        if (h == 0 && query < M) p.delta[qr + query] = dl;
+    }
 
     // K/V tiles [t0, t0 + n_kv): from the first key the workgroup's first row
     // sees to the last key its last row sees; the wave needs [w0, w1) of them
@@ -1430,7 +1429,7 @@ fa2_bwd_dq_f32_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 struct BwdEntry {
     int dtype, D, mask;
-    const void* delta;
+    const void* delta;  // Delta kernel (fp32); null: the dQ kernel computes Delta
     const void* dkdv;
     const void* dq;
     int kv_threads, kv_block_n, kv_block_q;  // dK/dV kernel: threads, keys per workgroup, query tile
@@ -1445,11 +1444,11 @@ struct BwdEntry {
 // waves per 128 keys), since K, V, dK and dV of 32 keys in VGPRs would leave
 // room for only one wave per SIMD.
 #define BWD_ROW64(E, code, mask)                                                                   \
-    {code, 64, mask, BWD_KERNEL(fa2_bwd_delta_kernel<E, 64>),                                    \
+    {code, 64, mask, nullptr,                                                                     \
      BWD_KERNEL(fa2_bwd_dkdv_kernel<E, 64, 64, 4, 2, mask>),                                     \
      BWD_KERNEL(fa2_bwd_dq_kernel<E, 64, 64, 4, 2, mask>), 256, 128, 64, 256, 128, 64, 4 * 8}
 #define BWD_ROW128(E, code, mask)                                                                  \
-    {code, 128, mask, BWD_KERNEL(fa2_bwd_delta_kernel<E, 128>),                                  \
+    {code, 128, mask, nullptr,                                                                    \
      BWD_KERNEL(fa2_bwd_dkdv_pair_kernel<E, 128, mask>),                                         \
      BWD_KERNEL(fa2_bwd_dq_kernel<E, 128, 32, 4, 2, mask>), 512, 128, 64, 256, 128, 32, 4 * 4}
 #define BWD_ROWS(E, code, mask) BWD_ROW64(E, code, mask), BWD_ROW128(E, code, mask)
@@ -1513,29 +1512,41 @@ bool bwd_outputs_overlap(const void* q, const void* k, const void* v, const void
     return false;
 }
 
-// The three launches: delta over `rows` rows, then dK/dV over n_kt key tiles
-// of every K/V head, then dQ over n_qt query tiles of every query head (the
-// kernel view's BH).
+// The launches.  fp32: Delta over `rows` rows, dK/dV over n_kt key tiles of
+// every K/V head, dQ over n_qt query tiles of every query head (the kernel
+// view's BH).  16-bit: dQ first, which also stores Delta, then dK/dV.
 int bwd_launch(const BwdEntry* e, BwdParams prm, int64_t rows, int64_t n_kt, int64_t n_qt_kv, int64_t n_qt,
-               const void* o, const void* dout, float* delta, hipStream_t st) {
+               hipStream_t st) {
     hipError_t err = hipSuccess;
-    if (rows > 0) {
-        const void* o_arg = o;
-        const void* do_arg = dout;
-        float* d_arg = delta;
-        int r = (int)rows;
-        void* dargs[] = {(void*)&o_arg, (void*)&do_arg, &d_arg, &r};
-        err = hipLaunchKernel(e->delta, dim3((unsigned)ceil_div(rows, e->delta_rows_per_wg)), dim3(256), dargs, 0, st);
-    }
-    if (err == hipSuccess && n_kt * prm.BHk > 0) {
-        prm.n_qt = (int)n_qt_kv;
-        void* args[] = {&prm};
+    auto launch_dkdv = [&]() {
+        if (err != hipSuccess || n_kt * prm.BHk <= 0) return;
+        BwdParams a = prm;
+        a.n_qt = (int)n_qt_kv;
+        void* args[] = {&a};
         err = hipLaunchKernel(e->dkdv, dim3((unsigned)(n_kt * prm.BHk)), dim3(e->kv_threads), args, 0, st);
-    }
-    if (err == hipSuccess && rows > 0 && n_qt * prm.BH > 0) {
-        prm.n_qt = (int)n_qt;
-        void* args[] = {&prm};
+    };
+    auto launch_dq = [&]() {
+        if (err != hipSuccess || rows <= 0 || n_qt * prm.BH <= 0) return;
+        BwdParams a = prm;
+        a.n_qt = (int)n_qt;
+        void* args[] = {&a};
         err = hipLaunchKernel(e->dq, dim3((unsigned)(n_qt * prm.BH)), dim3(e->q_threads), args, 0, st);
+    };
+    if (e->delta) {
+        if (rows > 0) {
+            const void* o_arg = prm.o;
+            const void* do_arg = prm.dout;
+            float* d_arg = prm.delta;
+            int r = (int)rows;
+            void* dargs[] = {(void*)&o_arg, (void*)&do_arg, &d_arg, &r};
+            err = hipLaunchKernel(e->delta, dim3((unsigned)ceil_div(rows, e->delta_rows_per_wg)), dim3(256), dargs,
+                                  0, st);
+        }
+        launch_dkdv();
+        launch_dq();
+    } else {
+        launch_dq();
+        launch_dkdv();
     }
     return launch_status(err);
 }
@@ -1584,7 +1595,7 @@ extern "C" int fa2_bwd_local(const void* q, const void* k, const void* v, const 
     if (BHk == 0) return FA2_OK;  // no K/V rows: nothing to write
 
     BwdParams prm{};  // dense layout: cu_q = cu_k = null
-    prm.q = q; prm.k = k; prm.v = v; prm.dout = dout; prm.lse = lse; prm.delta = delta;
+    prm.q = q; prm.k = k; prm.v = v; prm.dout = dout; prm.o = o; prm.lse = lse; prm.delta = delta;
     prm.dq = dq; prm.dk = dk; prm.dv = dv;
     prm.BH = (int)ks.BH;
     prm.BHk = (int)BHk;
@@ -1597,8 +1608,7 @@ extern "C" int fa2_bwd_local(const void* q, const void* k, const void* v, const 
     prm.wr = (int)wr;
     prm.c_log2 = scale * kLog2e;
     prm.scale = scale;
-    return bwd_launch(e, prm, BH * M, n_kt, ceil_div(ks.M, e->kv_block_q), n_qt, o, dout, delta,
-                      static_cast<hipStream_t>(stream));
+    return bwd_launch(e, prm, BH * M, n_kt, ceil_div(ks.M, e->kv_block_q), n_qt, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -1650,7 +1660,7 @@ extern "C" int fa2_bwd_varlen(const void* q, const void* k, const void* v, const
     if (BHk == 0) return FA2_OK;
 
     BwdParams prm{};
-    prm.q = q; prm.k = k; prm.v = v; prm.dout = dout; prm.lse = lse; prm.delta = delta;
+    prm.q = q; prm.k = k; prm.v = v; prm.dout = dout; prm.o = o; prm.lse = lse; prm.delta = delta;
     prm.dq = dq; prm.dk = dk; prm.dv = dv;
     prm.cu_q = cu_seqlens_q;
     prm.cu_k = cu_seqlens_k;
@@ -1665,6 +1675,6 @@ extern "C" int fa2_bwd_varlen(const void* q, const void* k, const void* v, const
     prm.wr = (int)wr;
     prm.c_log2 = scale * kLog2e;
     prm.scale = scale;
-    return bwd_launch(e, prm, H * total_q, n_kt, ceil_div(max_seqlen_q, e->kv_block_q), n_qt, o, dout, delta,
+    return bwd_launch(e, prm, H * total_q, n_kt, ceil_div(max_seqlen_q, e->kv_block_q), n_qt,
                       static_cast<hipStream_t>(stream));
 }

@@ -50,7 +50,10 @@ __device__ __forceinline__ void copy_tile_to_lds(const void* head, const uint32_
                                                  int wave_u, int kt, int N, char* dst) {
     // the buffer covers one head's K (V): the range check backs up the clamp
     const auto rsrc = make_rsrc(head, N * kRowBytes);
-    const int kbase = kt * BN;
+    // (the tile index is the same in every lane; saying so keeps the tile
+    // offset in a scalar register where the compiler cannot prove it, which
+    // would otherwise turn each load into a loop over distinct offsets)
+    const int kbase = __builtin_amdgcn_readfirstlane(kt) * BN;
     const int soff = kbase * kRowBytes;
     char* wdst = dst + wave_u * kLoads * 1024;
     if (kbase + BN <= N) {
@@ -105,6 +108,9 @@ struct Half<__bf16> {
         const v2 one = {(__bf16)1.0f, (__bf16)1.0f};
         return __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
     }
+    static __device__ __forceinline__ float dot2(v2 a, v2 b, float acc) {  // acc + a.x b.x + a.y b.y
+        return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+    }
 };
 template <>
 struct Half<_Float16> {
@@ -117,6 +123,9 @@ struct Half<_Float16> {
     static __device__ __forceinline__ float sum2(v2 p, float acc) {
         const v2 one = {(_Float16)1.0f, (_Float16)1.0f};
         return __builtin_amdgcn_fdot2(p, one, acc, false);
+    }
+    static __device__ __forceinline__ float dot2(v2 a, v2 b, float acc) {
+        return __builtin_amdgcn_fdot2(a, b, acc, false);
     }
 };
 
