@@ -23,7 +23,7 @@ non-causal).  Prints ONE JSON line with the whole-job throughput
   the tiny configuration on a single core;
 * workloads: per-launch latency (median of 100 after 25 warm-ups, with and
   without an L2/MALL flush before each launch) of every workload;
-* backward: per-call latency of fa2_bwd (delta, dK/dV and dQ kernels) on the
+* backward: per-call latency of fa2_bwd (its dQ, dK/dV and, for fp32, Delta kernels) on the
   workloads of workloads.BACKWARD, counted as 10*B*H*M*N*D flop (halved for
   causal).
 
@@ -576,7 +576,7 @@ def main(argv=None):
                 round(tf / (PEAK_TFLOPS[wx.dtype] * mhz / 2400.0), 4) if mhz else None)
             del bx, fx
         result["workloads"] = table
-        # backward passes (one fa2_bwd call each: delta, dK/dV, dQ kernels)
+        # backward passes (one fa2_bwd call each)
         btable = {}
         for name in workloads.BACKWARD:
             wx = workloads.get(name)

@@ -305,7 +305,8 @@ int fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* 
  * element (q, o, lse, dout, dq, delta when B*H*M == 0; k, v, dk, dv when
  * B == 0).
  *
- * Execution: three kernels on `stream` (delta; dK and dV; dQ), no
+ * Execution: on `stream`, for bf16 / fp16 two kernels (dQ, which also
+ * computes delta; then dK and dV), for fp32 three (delta; dK and dV; dQ); no
  * synchronisation; every output element is written exactly once, by one
  * workgroup, so results are identical run to run.  M == 0 writes dk = dv = 0;
  * B * Hk == 0 launches nothing.  Errors as for fa2_fwd: every argument check
