@@ -1120,35 +1120,72 @@ fa2_fwd_f32_kernel(const FwdParams p) {
                 }
         }
 
-        float mx = -INFINITY;
+        // Two ways to the weights.  Eager (the three-waves-per-SIMD form,
+        // 32-key tiles at D = 64): the tile's row max first; the running max
+        // moves (and O, l are rescaled) only when some row's max grew by more
+        // than 8 in log2 units, so the weights stay below 2^8.  Lazy (every
+        // other form): the weights are taken against the running max as it
+        // stands, and only when a lane's sum leaves [0, 2^64] (a weight above
+        // that, an inf, or the NaN of a row with no max yet) is the tile's
+        // row max taken, O and l rescaled and the weights recomputed.  fp32
+        // O and l hold weights up to 2^64 as accurately as weights up to 1
+        // (relative formats; the key that last set the max has weight 1, so
+        // l >= 1).  The lazy form keeps the weights beside the scores (16
+        // more live registers), which at three waves per SIMD cost more than
+        // the max it saves.
+        constexpr bool kEagerMax = D == 64 && BN == 32;
+        float lsum = -1.f;
+        if constexpr (!kEagerMax) {
+            auto weights = [&]() __attribute__((always_inline)) {
+                float w[T::kKB][16];
 #pragma unroll
-        for (int kb = 0; kb < T::kKB; ++kb)
+                for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-        mx = fmaxf(mx, xchg_half(mx));
-        // The running max moves (and O, l are rescaled) only when some row's
-        // max grew by more than 8 in log2 units; otherwise the weights stay
-        // below 2^8, which fp32 holds as accurately.
-        const float m_tile = mx * c_log2;
-        if (__any(m_tile > m_run + 8.f)) {
-            __asm__ volatile("");  // a rarely taken branch, not selects
-            const float m_new = fmaxf(m_run, m_tile);
-            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
+                    for (int r = 0; r < 16; ++r) w[kb][r] = fast_exp2(fmaf(sacc[kb][r], c_log2, -m_run));
+                float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int db = 0; db < T::kDB; ++db) oacc[db] *= alpha;
+                for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) l4[r & 3] += w[kb][r];
+                const float e = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+                if (__any(!(e <= 0x1p64f))) return -1.f;  // (not ">": NaN must fail too)
+#pragma unroll
+                for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[kb][r] = w[kb][r];
+                return e;
+            };
+            lsum = weights();
         }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float lsum = 0.f;
+        if (lsum < 0.f) {
+            if constexpr (!kEagerMax) __asm__ volatile("");  // a rarely taken branch, not selects
+            float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < T::kKB; ++kb)
+            for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float pw = fast_exp2(fmaf(sacc[kb][r], c_log2, -m_use));
-                sacc[kb][r] = pw;
-                lsum += pw;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+            mx = fmaxf(mx, xchg_half(mx));
+            const float m_tile = mx * c_log2;
+            if (!kEagerMax || __any(m_tile > m_run + 8.f)) {
+                __asm__ volatile("");  // a rarely taken branch, not selects
+                const float m_new = fmaxf(m_run, m_tile);
+                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db) oacc[db] *= alpha;
             }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            lsum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pw = fast_exp2(fmaf(sacc[kb][r], c_log2, -m_use));
+                    sacc[kb][r] = pw;
+                    lsum += pw;
+                }
+        }
         l_run += lsum;
 
         // O^T += V^T P^T: MFMA step r contracts key acc_row(r, h) in each half
