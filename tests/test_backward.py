@@ -240,3 +240,39 @@ def test_backward_varlen(causal, window, lens, D, dtype):
     got = tuple(t.float().cpu().numpy().astype(np.float64) for t in grads)
     ref = oracle.attention_bwd_varlen(q, k, v, do, cq, ck, 1.0 / math.sqrt(D), causal, window)
     compare_grads(got, ref, dtype, what)
+
+
+# Delta, the row correction of dS = P (dP - Delta), is part of fa2_bwd's
+# output: rowsum(dO o O) over the O the forward stored.  For 16-bit inputs the
+# dQ kernel computes it (from the dO it holds and one read of O) and stores it
+# for the dK/dV kernel; fp32 has a kernel of its own.  Every row must be
+# written (the buffer starts as NaN), and each value is a fp32 sum of D exact
+# products, so it is within D ulps of the fp64 sum of their magnitudes.
+@pytest.mark.parametrize("dtype,D,causal,H,Hk,M,N,window", [
+    ("bf16", 128, True, 4, 4, 300, 300, (-1, -1)),
+    ("bf16", 64, False, 6, 2, 257, 129, (-1, -1)),
+    ("f16", 128, False, 2, 1, 77, 500, (-1, -1)),
+    ("bf16", 128, True, 2, 2, 333, 333, (40, 0)),
+    ("f32", 64, True, 2, 2, 130, 130, (-1, -1)),
+])
+def test_backward_writes_delta_as_rowsum_dout_o(dtype, D, causal, H, Hk, M, N, window):
+    what = f"delta {dtype} D={D} causal={causal} H={H} Hk={Hk} M={M} N={N} window={window}"
+    note("case " + what)
+    B = 2
+    q, k, v = workloads.make_inputs(B, H, M, N, D, dtype, 11, 1.0, Hk=Hk)
+    do = workloads.make_dout(B, H, M, D, dtype, 11)
+    q, k, v, do = (t.to("cuda") for t in (q, k, v, do))
+    o, lse = fa2.forward(q, k, v, causal=causal, window=window)
+    delta = torch.full((B, H, M), float("nan"), dtype=torch.float32, device="cuda")
+    fa2.backward(q, k, v, o, lse, do, causal=causal, delta=delta, window=window)
+    torch.cuda.synchronize()
+    o64 = o.float().cpu().numpy().astype(np.float64)
+    do64 = do.float().cpu().numpy().astype(np.float64)
+    ref = (o64 * do64).sum(axis=-1)
+    mag = np.abs(o64 * do64).sum(axis=-1)
+    got = delta.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), f"{what}: rows of delta not written"
+    err = np.abs(got - ref)
+    bound = D * 2.0 ** -23 * mag + 1e-30
+    assert (err <= bound).all(), f"{what}: max excess {float((err - bound).max()):.3e}"
+    note(f"{what}: max|d delta|={float(err.max()):.2e}")
