@@ -595,7 +595,7 @@ fa2_fwd_half_kernel(const FwdParams p) {
 // the two are interleaved instruction by instruction; the MFMA of one wave
 // and the VALU of another wave on the same SIMD overlap without that.  This
 // kernel runs two groups of four waves (waves w and w + 4 share a SIMD) half
-// a tile out of phase, separated by workgroup barriers:
+// a tile out of phase:
 //
 //   period:     0        1        2          3          4 ...
 //   group A:  S(0)     sm(0)    PV(0)+S(1)  sm(1)      PV(1)+S(2)
@@ -607,11 +607,16 @@ fa2_fwd_half_kernel(const FwdParams p) {
 //
 // K_t is read in periods 2t (A) and 2t+1 (B), V_t in 2t+2 (A) and 2t+3 (B).
 // At the start of each even period 2t every wave issues its share of the
-// copies of K_{t+1} and V_t; it waits for them before the barrier that ends
-// period 2t+1, one period before they are read.  K_t and V_t live in buffer
-// t % 2; the loop is unrolled over four periods so that every LDS access
-// names its buffer statically and the compiler can see that the copies in
-// flight never alias the buffers being read.
+// copies of K_{t+1} and V_t; it waits for them before the workgroup barrier
+// that ends period 2t+1, one period before they are read.  That barrier, one
+// per tile, is the only one: it publishes those copies and retires the reads
+// of K_t and V_{t-1}, whose buffers the next copies overwrite; between two
+// barriers group A runs its MFMA phase then its softmax, group B its softmax
+// then its MFMA phase, with nothing to keep them in step (a barrier there
+// would guard no buffer).  K_t and V_t live in buffer t % 2; the loop is
+// unrolled over four periods so that every LDS access names its buffer
+// statically and the compiler can see that the copies in flight never alias
+// the buffers being read.
 //
 // Each wave owns 32 query rows; group A takes the even 32-row blocks of the
 // workgroup's 256 rows and group B the odd ones, so under a causal mask the
@@ -898,7 +903,6 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
         if (t0 < n_kv) issue_copy(Vh, cp_voff, t0, sV0);
         if (grp == 0) mfma_phase(t0, sK0, sV1);
         else valu_phase(t0 - 1);
-        lds_barrier();
         // period p0+1: B: PV(t0-1) [V buf 1] + S(t0) [K buf 0];  A: sm(t0)
         if (grp == 1) mfma_phase(t0, sK0, sV1);
         else valu_phase(t0);
@@ -910,7 +914,6 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
         if (t0 + 1 < n_kv) issue_copy(Vh, cp_voff, t0 + 1, sV1);
         if (grp == 0) mfma_phase(t0 + 1, sK1, sV0);
         else valu_phase(t0);
-        lds_barrier();
         // period p0+3: B: PV(t0) [V buf 0] + S(t0+1) [K buf 1];  A: sm(t0+1)
         if (grp == 1) mfma_phase(t0 + 1, sK1, sV0);
         else valu_phase(t0 + 1);
