@@ -523,12 +523,17 @@ fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
     E* __restrict__ dK = static_cast<E*>(p.dk);
     E* __restrict__ dV = static_cast<E*>(p.dv);
     const float c_log2 = p.c_log2;
-    __shared__ __attribute__((aligned(1024))) char sK[T::kKTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sV[T::kKTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sQ0[T::kQTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sO0[T::kQTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sQ1[T::kQTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sO1[T::kQTileBytes];
+    // The Q/dO buffers are read twice per row block (as rows and transposed)
+    // and carry the larger alignment, which places them first, below 64 KiB,
+    // where their bases fit the DS instructions' 16-bit offset field; K and V
+    // share one array so that V is K plus a constant offset.
+    __shared__ __attribute__((aligned(T::kQTileBytes))) char sQ0[T::kQTileBytes];
+    __shared__ __attribute__((aligned(T::kQTileBytes))) char sO0[T::kQTileBytes];
+    __shared__ __attribute__((aligned(T::kQTileBytes))) char sQ1[T::kQTileBytes];
+    __shared__ __attribute__((aligned(T::kQTileBytes))) char sO1[T::kQTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sKV[2 * T::kKTileBytes];
+    char* const sK = sKV;
+    char* const sV = sKV + T::kKTileBytes;
     __shared__ __attribute__((aligned(16))) float sL0[T::kBQ], sL1[T::kBQ], sD0[T::kBQ], sD1[T::kBQ];
 
     const int tid = threadIdx.x;
@@ -567,8 +572,26 @@ fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
     copy_offsets<D, T::kKLoads>(k_off, wave, lane);
     TileReads<D> rd;
     rd.init(lane);
-    const char* kq = sK + 32 * kb * T::kRowBytes;  // this wave's key rows (B operands)
-    const char* vq = sV + 32 * kb * T::kRowBytes;
+    // per-lane read offsets with the wave's row block folded in (the wave
+    // index is uniform, but a value derived from the thread index is treated
+    // as per-lane; folding it here keeps an add off every read)
+    int q_row[T::kDS], k_row[T::kDS], q_tr_lo[T::kDB], q_tr_hi[T::kDB];
+#pragma unroll
+    for (int s = 0; s < T::kDS; ++s) {
+        q_row[s] = 32 * qb * T::kRowBytes + rd.row_off[s];
+        k_row[s] = 32 * kb * T::kRowBytes + rd.row_off[s];
+    }
+#pragma unroll
+    for (int db = 0; db < T::kDB; ++db) {
+        q_tr_lo[db] = 32 * qb * T::kRowBytes + rd.tr_lo[db];
+        q_tr_hi[db] = 32 * qb * T::kRowBytes + rd.tr_hi[db];
+    }
+    auto tr_read = [&](const char* tile, int ms, int db) {
+        const char* p = tile + 16 * ms * T::kRowBytes;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + q_tr_lo[db]));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + q_tr_hi[db]));
+        return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 
     auto tile_head = [&](int it, int& bh, int& qt) {
         const int g = it / per_g;
@@ -609,10 +632,10 @@ fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
         floatx16 sacc = floatx16{}, pacc = floatx16{};
 #pragma unroll
         for (int s = 0; s < T::kDS; ++s) {
-            const V8 qa = rd.template row<V8>(qs, qb, s);
-            const V8 oa = rd.template row<V8>(os, qb, s);
-            const V8 kf = rd.template row<V8>(kq, 0, s);
-            const V8 vf = rd.template row<V8>(vq, 0, s);
+            const V8 qa = *reinterpret_cast<const V8*>(qs + q_row[s]);
+            const V8 oa = *reinterpret_cast<const V8*>(os + q_row[s]);
+            const V8 kf = *reinterpret_cast<const V8*>(sK + k_row[s]);
+            const V8 vf = *reinterpret_cast<const V8*>(sV + k_row[s]);
             sacc = Half<E>::mfma(qa, kf, sacc);
             pacc = Half<E>::mfma(oa, vf, pacc);
         }
@@ -643,8 +666,8 @@ fa2_bwd_dkdv_pair_kernel(const BwdParams p) {
             const V8 sb = __builtin_bit_cast(V8, u32x4{sw[ms][0], sw[ms][1], sw[ms][2], sw[ms][3]});
 #pragma unroll
             for (int db = 0; db < T::kDB; ++db) {
-                const V8 oa = rd.template tr<V8>(os, 2 * qb + ms, db);
-                const V8 qa = rd.template tr<V8>(qs, 2 * qb + ms, db);
+                const V8 oa = tr_read(os, ms, db);
+                const V8 qa = tr_read(qs, ms, db);
                 dvacc[db] = Half<E>::mfma(oa, pb, dvacc[db]);
                 dkacc[db] = Half<E>::mfma(qa, sb, dkacc[db]);
             }
