@@ -884,20 +884,39 @@ fa2_bwd_dq_kernel(const BwdParams p) {
         floatx16 sacc[T::kKB], pacc[T::kKB];
 #pragma unroll
         for (int kb = 0; kb < T::kKB; ++kb) sacc[kb] = pacc[kb] = floatx16{};
+        // K and V operands read from LDS two steps ahead of their MFMAs (the
+        // scheduling fences keep the reads from sinking next to their uses)
+        constexpr int kSteps = T::kDS * T::kKB;
+        constexpr int kAhead = 2;
+        V8 kr[kAhead + 1], vr[kAhead + 1];
 #pragma unroll
-        for (int s = 0; s < T::kDS; ++s) {
-            V8 ka[T::kKB], va[T::kKB];
-#pragma unroll
-            for (int kb = 0; kb < T::kKB; ++kb) {
-                ka[kb] = rd.template row<V8>(ks, kb, s);
-                va[kb] = rd.template row<V8>(vs, kb, s);
-            }
-#pragma unroll
-            for (int kb = 0; kb < T::kKB; ++kb) {
-                sacc[kb] = Half<E>::mfma(ka[kb], qf[s], sacc[kb]);
-                pacc[kb] = Half<E>::mfma(va[kb], of[s], pacc[kb]);
-            }
+        for (int i = 0; i < kAhead; ++i) {
+            kr[i] = rd.template row<V8>(ks, i % T::kKB, i / T::kKB);
+            vr[i] = rd.template row<V8>(vs, i % T::kKB, i / T::kKB);
         }
+#pragma unroll
+        for (int i = 0; i < kSteps; ++i) {
+            if (i + kAhead < kSteps) {
+                const int j = i + kAhead;
+                kr[j % (kAhead + 1)] = rd.template row<V8>(ks, j % T::kKB, j / T::kKB);
+                vr[j % (kAhead + 1)] = rd.template row<V8>(vs, j % T::kKB, j / T::kKB);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const int s = i / T::kKB, kb = i % T::kKB;
+            sacc[kb] = Half<E>::mfma(kr[i % (kAhead + 1)], qf[s], sacc[kb]);
+            pacc[kb] = Half<E>::mfma(vr[i % (kAhead + 1)], of[s], pacc[kb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the A operands of dQ^T += K^T dS^T, read now so that their latency
+        // passes during the softmax-gradient work below
+        V8 kt_a[T::kKB][2][T::kDB];
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db) kt_a[kb][ms][db] = rd.template tr<V8>(ks, 2 * kb + ms, db);
+        __builtin_amdgcn_sched_barrier(0);
         // boundary tiles only: keys past N, or outside some row's causal or
         // window range; key kbase + 32 kb + acc_row(r, h) is visible iff its
         // compile-time part lies in [lim_lo, lim]
@@ -930,11 +949,8 @@ fa2_bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
             for (int ms = 0; ms < 2; ++ms) {
                 const V8 sb = __builtin_bit_cast(V8, u32x4{sw[kb][ms][0], sw[kb][ms][1], sw[kb][ms][2], sw[kb][ms][3]});
-                V8 ka[T::kDB];
 #pragma unroll
-                for (int db = 0; db < T::kDB; ++db) ka[db] = rd.template tr<V8>(ks, 2 * kb + ms, db);
-#pragma unroll
-                for (int db = 0; db < T::kDB; ++db) dqacc[db] = Half<E>::mfma(ka[db], sb, dqacc[db]);
+                for (int db = 0; db < T::kDB; ++db) dqacc[db] = Half<E>::mfma(kt_a[kb][ms][db], sb, dqacc[db]);
             }
     };
 
