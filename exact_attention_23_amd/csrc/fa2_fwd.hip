@@ -735,12 +735,32 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
     // (the scheduling fences keep the compiler from sinking the reads next
     // to their uses).  PV(-1) multiplies a zero P by a zero-filled V buffer;
     // the S(n_w) of a wave's last MFMA phase is computed and discarded, so
-    // every phase runs the same straight-line code.  After its MFMAs the
-    // phase adds the rounded weights of P(t-1) to l_run (two per v_dot2
-    // against (1, 1)): work taken out of the softmax phase, which sets the
-    // period, and done while the partner wave issues no MFMAs.
+    // every phase runs the same straight-line code.  The phase also adds the
+    // rounded weights of P(t-1) to l_run (two per v_dot2 against (1, 1)):
+    // work taken out of the softmax phase, done while the partner wave
+    // issues no MFMAs.  At D = 128 half of those sums run while the first
+    // operand reads are in flight and half after the MFMAs; at D = 64 (a
+    // phase of 16 MFMAs) all run after them.
     constexpr int kSteps = T::kDS * T::kKB;  // == number of PV MFMAs
     static_assert(kSteps == T::kKB * 2 * T::kDB, "one PV and one S MFMA per step");
+    constexpr int kSumsFirst = D == 128 ? 1 : 0;  // halves ms of pf summed ahead of the MFMAs (bit ms)
+    auto sum_rounded = [&](int halves) {
+        if (halves == 0) return;
+        float ls0 = l_run, ls1 = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < T::kKB; ++kb)
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms) {
+                if (!((halves >> ms) & 1)) continue;
+#pragma unroll
+                for (int u = 0; u < 8; u += 2) {
+                    const V2 pp = {pf[kb][ms][u], pf[kb][ms][u + 1]};
+                    if ((u >> 1) & 1) ls1 = Half<E>::sum2(pp, ls1);
+                    else ls0 = Half<E>::sum2(pp, ls0);
+                }
+            }
+        l_run = ls0 + ls1;
+    };
     auto read_v = [&](const char* vprev, int i) {
         const int step = i / T::kDB, db = i % T::kDB;
         const char* p0 = vprev + 16 * step * T::kRowBytes + v_lane_off[db];
@@ -763,6 +783,11 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
             vr[i] = read_v(vprev, i);
             kr[i] = read_k(klds, i);
         }
+        if constexpr (kSumsFirst != 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            sum_rounded(kSumsFirst);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int i = 0; i < kSteps; ++i) {
             if (i + kAhead < kSteps) {
@@ -781,18 +806,7 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        float ls0 = l_run, ls1 = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < T::kKB; ++kb)
-#pragma unroll
-            for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-                for (int u = 0; u < 8; u += 2) {
-                    const V2 pp = {pf[kb][ms][u], pf[kb][ms][u + 1]};
-                    if ((u >> 1) & 1) ls1 = Half<E>::sum2(pp, ls1);
-                    else ls0 = Half<E>::sum2(pp, ls0);
-                }
-        l_run = ls0 + ls1;
+        sum_rounded(3 & ~kSumsFirst);
     };
 
     // ---- VALU phase: mask (boundary tiles), online softmax, rescale.
