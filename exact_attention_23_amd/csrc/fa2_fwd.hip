@@ -616,7 +616,10 @@ fa2_fwd_half_kernel(const FwdParams p) {
 // would guard no buffer).  K_t and V_t live in buffer t % 2; the loop is
 // unrolled over four periods so that every LDS access names its buffer
 // statically and the compiler can see that the copies in flight never alias
-// the buffers being read.
+// the buffers being read.  The four buffers (64 KiB at D = 128) fill the
+// bottom of LDS, so each buffer's base fits a DS instruction's 16-bit
+// immediate offset and an operand read is a single instruction; a buffer
+// above 64 KiB would cost an address add per read, in the MFMA phase.
 //
 // Each wave owns 32 query rows; group A takes the even 32-row blocks of the
 // workgroup's 256 rows and group B the odd ones, so under a causal mask the
