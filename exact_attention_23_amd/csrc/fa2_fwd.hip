@@ -623,7 +623,10 @@ fa2_fwd_half_kernel(const FwdParams p) {
 //
 // Each wave owns 32 query rows; group A takes the even 32-row blocks of the
 // workgroup's 256 rows and group B the odd ones, so under a causal mask the
-// two waves of a SIMD need the same number of tiles (to within one).
+// two waves of a SIMD need the same number of tiles (to within one).  The
+// kernel serves the dense, sliding-window and packed-sequence calls: under a
+// window a wave's rows see keys from tile w_first on, and the tiles before
+// it give P = 0 without a softmax.
 template <int D, int BN>
 struct PPTraits {
     static constexpr int kNW = 8;
@@ -642,7 +645,7 @@ struct PPTraits {
     static_assert(kTileChunks % (64 * kNW) == 0, "loader split");
 };
 
-template <typename E, int D, int BN, bool CAUSAL, bool SPLIT>
+template <typename E, int D, int BN, int MASK, bool SPLIT>
 __global__ void __launch_bounds__(512, 2)
 fa2_fwd_half_pp_kernel(const FwdParams p) {
     using T = PPTraits<D, BN>;
@@ -653,7 +656,6 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
     const E* __restrict__ V = static_cast<const E*>(p.v);
     E* __restrict__ O = static_cast<E*>(p.o);
     float* __restrict__ LSE = p.lse;
-    const int M = p.M, N = p.N;
     const float c_log2 = p.c_log2;
     __shared__ __attribute__((aligned(1024))) char sK0[T::kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV0[T::kTileBytes];
@@ -667,20 +669,23 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
-    // (dense layout and no window: the ping-pong kernel serves fa2_fwd_ex only)
-    constexpr int MASK = CAUSAL ? kMaskCausal : kMaskNone;
+    // the workgroup's sequence: a head of the dense layout or one packed
+    // sequence; any mask kind (none, causal, sliding window)
     const WgTask task = wg_task<MASK, SPLIT>(p, T::kBM, BN);
-    const int bh = task.bh;
+    const int M = task.sv.M, N = task.sv.N;
     const int qw0 = task.qt * T::kBM + 32 * (2 * (wave & 3) + grp);  // first query row of this wave
+    const int qw1 = min(qw0 + 32, M) - 1;                             // its last one
 
-    const E* Qh = Q + (int64_t)bh * M * D;
-    const E* Kh = K + (int64_t)task.bkv * N * D;
-    const E* Vh = V + (int64_t)task.bkv * N * D;
+    const E* Qh = Q + task.sv.q_row0 * D;
+    const E* Kh = K + task.sv.kv_row0 * D;
+    const E* Vh = V + task.sv.kv_row0 * D;
 
-    // local tile t is K/V tile kv_t0 + t of the head
+    // local tile t is K/V tile kv_t0 + t of the head; the wave's rows see
+    // keys in tiles [w_first, n_w) only (w_first > 0 under a window)
     const int kv_t0 = task.t_begin;
     const int n_kv = task.n_kv;
-    const int n_w = wave_tiles<MASK>(p, task, qw0, 32, BN).end;  // tiles this wave needs (from tile 0)
+    const WaveRange w_range = wave_tiles<MASK>(p, task, qw0, 32, BN);
+    const int n_w = w_range.end, w_first = w_range.first;
 
     // ---- Q fragments: B operand of S^T = K Q^T (lane = query, 8 d values)
     V8 qf[T::kDS];
@@ -861,17 +866,28 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
     };
     auto valu_phase = [&](int t) {
         if (t < 0 || t >= n_w) return;
+        if (MASK == kMaskLocal && t < w_first) {
+            // a tile before the window of every row of the wave: P = 0, so
+            // the PV product of the next MFMA phase adds nothing
+#pragma unroll
+            for (int kb = 0; kb < T::kKB; ++kb) pf[kb][0] = pf[kb][1] = V8{};
+            return;
+        }
         const int kbase = (kv_t0 + t) * BN;
-        if (kbase + BN > N || (CAUSAL && kbase + BN - 1 > qw0)) {
+        if (tile_needs_mask<MASK>(p, kbase, BN, N, qw0, qw1)) {
             __asm__ volatile("");  // keep this a branch, not a select per element
-            int lim = N - 1 - kbase;
-            if (CAUSAL) lim = min(lim, qw0 + l32 - kbase);
-            lim -= 4 * h;
+            // key kbase + 32 kb + acc_row(r, h) is visible iff its
+            // compile-time part 32 kb + 8 (r / 4) + r % 4 lies in [lim_lo, lim]
+            const int query = qw0 + l32;
+            const int lim = key_hi<MASK>(p, query, N) - kbase - 4 * h;
+            const int lim_lo = key_lo<MASK>(p, query) - kbase - 4 * h;
 #pragma unroll
             for (int kb = 0; kb < T::kKB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const int idx = 32 * kb + 8 * (r >> 2) + (r & 3);
+                    if (idx > lim || (MASK == kMaskLocal && idx < lim_lo)) sacc[kb][r] = -INFINITY;
+                }
         }
         float e_tile = weights(m_run);
         if (__any(!(e_tile <= Half<E>::kWeightSumCap))) {  // (not ">": NaN must fail too)
@@ -983,14 +999,14 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave reads back its own writes
             constexpr int kRowsPerRead = 64 / T::kCPR;
             const int rr = lane / T::kCPR, cc = lane % T::kCPR;
-            E* const obase = O + ((int64_t)bh * M + qw0) * D;
+            E* const obase = O + (task.sv.q_row0 + qw0) * D;
 #pragma unroll
             for (int i = 0; i < 32 / kRowsPerRead; ++i) {
                 const int r = i * kRowsPerRead + rr;
                 const uint4 x = *reinterpret_cast<const uint4*>(stage + r * T::kRowBytes + 16 * (cc ^ (r % T::kCPR)));
                 if (qw0 + r < M) *reinterpret_cast<uint4*>(obase + (int64_t)r * D + 8 * cc) = x;
             }
-            if (h == 0 && query < M) LSE[(int64_t)bh * M + query] = lse;
+            if (h == 0 && query < M) LSE[task.sv.q_row0 + query] = lse;
         }
     }
 }
@@ -1444,8 +1460,8 @@ struct LocalEntry {
     int block_m;  // query rows per workgroup
 };
 #define LOCAL_HALF(E, code, mask)                                                                      \
-    {code, 64, mask, FWD_KERNEL(fa2_fwd_half_kernel<E, 64, 128, 8, 1, 2, mask, false>), 512, 256},     \
-    {code, 128, mask, FWD_KERNEL(fa2_fwd_half_kernel<E, 128, 64, 8, 1, 2, mask, false>), 512, 256}
+    {code, 64, mask, FWD_KERNEL(fa2_fwd_half_pp_kernel<E, 64, 64, mask, false>), 512, 256},            \
+    {code, 128, mask, FWD_KERNEL(fa2_fwd_half_pp_kernel<E, 128, 64, mask, false>), 512, 256}
 #define LOCAL_F32(mask)                                                                                \
     {FA2_DTYPE_F32, 64, mask, FWD_KERNEL(fa2_fwd_f32_kernel<64, 64, 4, mask, false>), 256, 128},        \
     {FA2_DTYPE_F32, 128, mask, FWD_KERNEL(fa2_fwd_f32_kernel<128, 32, 4, mask, false>), 256, 128}
