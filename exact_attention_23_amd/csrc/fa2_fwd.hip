@@ -673,6 +673,10 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
     // sequence; any mask kind (none, causal, sliding window)
     const WgTask task = wg_task<MASK, SPLIT>(p, T::kBM, BN);
     const int M = task.sv.M, N = task.sv.N;
+    // a query tile past its sequence's rows (packed sequences shorter than
+    // the longest): nothing to compute or store; the condition is the same
+    // for every wave of the workgroup, so no barrier is left waiting
+    if (task.qt * T::kBM >= M) return;
     const int qw0 = task.qt * T::kBM + 32 * (2 * (wave & 3) + grp);  // first query row of this wave
     const int qw1 = min(qw0 + 32, M) - 1;                             // its last one
 
