@@ -1375,14 +1375,14 @@ const Entry kTable[] = {
     // 64-key K/V tile, 256 query rows per workgroup.  At D = 64 it measured 5 %
     // faster than the plain 8-wave kernel (128-key tiles) on the ragged
     // cross-attention workload; 128-key ping-pong tiles gained nothing there.
-    {FA2_DTYPE_BF16, 64, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 64, 64, false), 512, 256, 64, 1},
-    {FA2_DTYPE_BF16, 64, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 64, 64, true), 512, 256, 64, 1},
-    {FA2_DTYPE_BF16, 128, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 128, 64, false), 512, 256, 64, 1},
-    {FA2_DTYPE_BF16, 128, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 128, 64, true), 512, 256, 64, 1},
-    {FA2_DTYPE_F16, 64, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 64, 64, false), 512, 256, 64, 1},
-    {FA2_DTYPE_F16, 64, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 64, 64, true), 512, 256, 64, 1},
-    {FA2_DTYPE_F16, 128, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, false), 512, 256, 64, 1},
-    {FA2_DTYPE_F16, 128, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, true), 512, 256, 64, 1},
+    {FA2_DTYPE_BF16, 64, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 64, 64, kMaskNone), 512, 256, 64, 1},
+    {FA2_DTYPE_BF16, 64, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 64, 64, kMaskCausal), 512, 256, 64, 1},
+    {FA2_DTYPE_BF16, 128, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 128, 64, kMaskNone), 512, 256, 64, 1},
+    {FA2_DTYPE_BF16, 128, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, __bf16, 128, 64, kMaskCausal), 512, 256, 64, 1},
+    {FA2_DTYPE_F16, 64, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 64, 64, kMaskNone), 512, 256, 64, 1},
+    {FA2_DTYPE_F16, 64, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 64, 64, kMaskCausal), 512, 256, 64, 1},
+    {FA2_DTYPE_F16, 128, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, kMaskNone), 512, 256, 64, 1},
+    {FA2_DTYPE_F16, 128, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, kMaskCausal), 512, 256, 64, 1},
     // fp32: 4 waves, 128 query rows; at D = 64 non-causal 32-key tiles with
     // three workgroups per CU measured ~2.5 % faster than 64-key tiles with
     // two, and ~10 % slower under a causal mask (twice the masked diagonal
@@ -1454,9 +1454,8 @@ int choose_splits(const Entry& e, int64_t BH, int64_t M, int64_t N) {
     return (int)std::max<int64_t>(1, s);
 }
 
-// Sliding-window and packed-sequence entry points: the general 8-wave 16-bit
-// kernel (the dense entry point uses the ping-pong kernel instead) and the
-// fp32 kernel, one instantiation per mask kind, unsplit.
+// Sliding-window and packed-sequence entry points: the ping-pong 16-bit
+// kernel and the fp32 kernel, one instantiation per mask kind, unsplit.
 struct LocalEntry {
     int dtype, D, mask;
     const void* kernel;
