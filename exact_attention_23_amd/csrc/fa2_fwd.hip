@@ -645,7 +645,7 @@ struct PPTraits {
     static_assert(kTileChunks % (64 * kNW) == 0, "loader split");
 };
 
-template <typename E, int D, int BN, int MASK, bool SPLIT>
+template <typename E, int D, int BN, int MASK, bool SPLIT, bool PACKED = false>
 __global__ void __launch_bounds__(512, 2)
 fa2_fwd_half_pp_kernel(const FwdParams p) {
     using T = PPTraits<D, BN>;
@@ -673,10 +673,14 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
     // sequence; any mask kind (none, causal, sliding window)
     const WgTask task = wg_task<MASK, SPLIT>(p, T::kBM, BN);
     const int M = task.sv.M, N = task.sv.N;
-    // a query tile past its sequence's rows (packed sequences shorter than
-    // the longest): nothing to compute or store; the condition is the same
-    // for every wave of the workgroup, so no barrier is left waiting
-    if (task.qt * T::kBM >= M) return;
+    // packed sequences: a query tile past its sequence's rows (sequences
+    // shorter than the longest) has nothing to compute or store; the
+    // condition is the same for every wave of the workgroup, so no barrier
+    // is left waiting.  (Compiled only into the packed form: in the others
+    // the test cost ~1 % on the dense shapes.)
+    if constexpr (PACKED) {
+        if (task.qt * T::kBM >= M) return;
+    }
     const int qw0 = task.qt * T::kBM + 32 * (2 * (wave & 3) + grp);  // first query row of this wave
     const int qw1 = min(qw0 + 32, M) - 1;                             // its last one
 
@@ -1457,17 +1461,21 @@ int choose_splits(const Entry& e, int64_t BH, int64_t M, int64_t N) {
 // Sliding-window and packed-sequence entry points: the ping-pong 16-bit
 // kernel and the fp32 kernel, one instantiation per mask kind, unsplit.
 struct LocalEntry {
-    int dtype, D, mask;
+    int dtype, D, mask, packed;  // packed: fa2_fwd_varlen's packed layout
     const void* kernel;
     int threads;
     int block_m;  // query rows per workgroup
 };
 #define LOCAL_HALF(E, code, mask)                                                                      \
-    {code, 64, mask, FWD_KERNEL(fa2_fwd_half_pp_kernel<E, 64, 64, mask, false>), 512, 256},            \
-    {code, 128, mask, FWD_KERNEL(fa2_fwd_half_pp_kernel<E, 128, 64, mask, false>), 512, 256}
+    {code, 64, mask, 0, FWD_KERNEL(fa2_fwd_half_pp_kernel<E, 64, 64, mask, false>), 512, 256},         \
+    {code, 128, mask, 0, FWD_KERNEL(fa2_fwd_half_pp_kernel<E, 128, 64, mask, false>), 512, 256},       \
+    {code, 64, mask, 1, FWD_KERNEL(fa2_fwd_half_pp_kernel<E, 64, 64, mask, false, true>), 512, 256},   \
+    {code, 128, mask, 1, FWD_KERNEL(fa2_fwd_half_pp_kernel<E, 128, 64, mask, false, true>), 512, 256}
 #define LOCAL_F32(mask)                                                                                \
-    {FA2_DTYPE_F32, 64, mask, FWD_KERNEL(fa2_fwd_f32_kernel<64, 64, 4, mask, false>), 256, 128},        \
-    {FA2_DTYPE_F32, 128, mask, FWD_KERNEL(fa2_fwd_f32_kernel<128, 32, 4, mask, false>), 256, 128}
+    {FA2_DTYPE_F32, 64, mask, 0, FWD_KERNEL(fa2_fwd_f32_kernel<64, 64, 4, mask, false>), 256, 128},     \
+    {FA2_DTYPE_F32, 128, mask, 0, FWD_KERNEL(fa2_fwd_f32_kernel<128, 32, 4, mask, false>), 256, 128},   \
+    {FA2_DTYPE_F32, 64, mask, 1, FWD_KERNEL(fa2_fwd_f32_kernel<64, 64, 4, mask, false>), 256, 128},     \
+    {FA2_DTYPE_F32, 128, mask, 1, FWD_KERNEL(fa2_fwd_f32_kernel<128, 32, 4, mask, false>), 256, 128}
 const LocalEntry kLocalTable[] = {
     LOCAL_HALF(__bf16, FA2_DTYPE_BF16, kMaskNone),  LOCAL_HALF(__bf16, FA2_DTYPE_BF16, kMaskCausal),
     LOCAL_HALF(__bf16, FA2_DTYPE_BF16, kMaskLocal), LOCAL_HALF(_Float16, FA2_DTYPE_F16, kMaskNone),
@@ -1477,9 +1485,9 @@ const LocalEntry kLocalTable[] = {
 #undef LOCAL_HALF
 #undef LOCAL_F32
 
-const LocalEntry* find_local_entry(int dtype, int64_t D, int mask) {
+const LocalEntry* find_local_entry(int dtype, int64_t D, int mask, int packed) {
     for (const LocalEntry& t : kLocalTable)
-        if (t.dtype == dtype && t.D == D && t.mask == mask) return &t;
+        if (t.dtype == dtype && t.D == D && t.mask == mask && t.packed == packed) return &t;
     return nullptr;
 }
 
@@ -1700,7 +1708,7 @@ extern "C" int fa2_fwd_local(const void* q, const void* k, const void* v, void* 
         return FA2_ERR_INVALID_ARGUMENT;
     int64_t wl = window_left, wr = window_right;
     const int mask = normalise_window(wl, wr, causal, M, N);
-    const LocalEntry* e = find_local_entry(dtype, D, mask);
+    const LocalEntry* e = find_local_entry(dtype, D, mask, 0);
     if (!e) return FA2_ERR_UNSUPPORTED;
     const int64_t n_qt = ceil_div(M, e->block_m);
     if (n_qt * BH >= kMax) return FA2_ERR_UNSUPPORTED;
@@ -1755,7 +1763,7 @@ extern "C" int fa2_fwd_varlen(const void* q, const void* k, const void* v, void*
         return FA2_ERR_INVALID_ARGUMENT;
     int64_t wl = window_left, wr = window_right;
     const int mask = normalise_window(wl, wr, causal, total_q, total_k);
-    const LocalEntry* e = find_local_entry(dtype, D, mask);
+    const LocalEntry* e = find_local_entry(dtype, D, mask, 1);
     if (!e) return FA2_ERR_UNSUPPORTED;
     const int64_t BH = B * H;
     const int64_t n_qt = ceil_div(max_seqlen_q, e->block_m);
