@@ -1402,9 +1402,9 @@ const Entry kTable[] = {
 // waves, one K/V tile double-buffered in 64 KiB of LDS, two workgroups per
 // CU), so that the split count that fills the GPU spreads the keys over more
 // workgroups and HBM, not the matrix core, sets the time.  (Their "two
-// waves per SIMD" bound only caps the registers at 256, as in the other
-// tables; LDS allows one wave per SIMD, so the compiler warns that the bound
-// is not met.  A bound of one wave lets it spread into AGPRs and copy.)
+// waves per SIMD" bound is not met -- they take 218-256 VGPRs and 96-142
+// AGPRs -- and the compiler warns; LDS allows one wave per SIMD anyway.  A
+// bound of one wave moved still more state into AGPRs, with copies.)
 constexpr int64_t kShortRows = 64;  // rows per (K/V) head up to which kShortTable serves
 const Entry kShortTable[] = {
     {FA2_DTYPE_BF16, 64, 0, FWD_PAIR(fa2_fwd_half_kernel, __bf16, 64, 128, 2, 1, 2, kMaskNone), 128, 64, 128, 2},
