@@ -872,6 +872,9 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
                 }
         return (esum[0] + esum[1]) + (esum[2] + esum[3]);
     };
+    // The phase runs at raised wave priority: where the two waves of a SIMD
+    // both have an instruction ready, the softmax's VALU issues ahead of the
+    // partner's MFMA (the softmax phase is the longer one; -2 % at D = 64).
     auto valu_phase = [&](int t) {
         if (t < 0 || t >= n_w) return;
         if (MASK == kMaskLocal && t < w_first) {
@@ -881,6 +884,7 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
             for (int kb = 0; kb < T::kKB; ++kb) pf[kb][0] = pf[kb][1] = V8{};
             return;
         }
+        __builtin_amdgcn_s_setprio(1);
         const int kbase = (kv_t0 + t) * BN;
         if (tile_needs_mask<MASK>(p, kbase, BN, N, qw0, qw1)) {
             __asm__ volatile("");  // keep this a branch, not a select per element
@@ -925,6 +929,7 @@ fa2_fwd_half_pp_kernel(const FwdParams p) {
             e_tile = weights(m_run == -INFINITY ? 0.f : m_run);
         }
         l_exact += e_tile;
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // ---- prologue: K_0 in buffer 0; V buffer 1 zeroed (read by PV(-1))
