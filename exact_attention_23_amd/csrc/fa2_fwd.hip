@@ -1155,6 +1155,11 @@ fa2_fwd_f32_kernel(const FwdParams p) {
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[u], qf[s + u], sacc[kb], 0, 0, 0);
             }
         }
+        // The softmax runs at raised wave priority: the three waves of a SIMD
+        // come from three workgroups, and issuing a wave's softmax ahead of
+        // the others' MFMAs gets its PV products and its workgroup's barrier
+        // sooner (-1.3 % at D = 64, -7 % causal; +-0 at D = 128).
+        __builtin_amdgcn_s_setprio(1);
 
         const int kbase = (kv_t0 + kt) * BN;
         if (tile_needs_mask<MASK>(p, kbase, BN, N, qw0, qw1)) {
@@ -1236,6 +1241,7 @@ fa2_fwd_f32_kernel(const FwdParams p) {
                 }
         }
         l_run += lsum;
+        __builtin_amdgcn_s_setprio(0);
 
         // O^T += V^T P^T: MFMA step r contracts key acc_row(r, h) in each half
 #pragma unroll
