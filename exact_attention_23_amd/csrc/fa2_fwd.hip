@@ -1399,8 +1399,8 @@ const Entry kTable[] = {
     {FA2_DTYPE_F16, 128, 0, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, kMaskNone), 512, 256, 64, 1},
     {FA2_DTYPE_F16, 128, 1, FWD_PAIR(fa2_fwd_half_pp_kernel, _Float16, 128, 64, kMaskCausal), 512, 256, 64, 1},
     // fp32: 4 waves, 128 query rows; at D = 64 non-causal 32-key tiles with
-    // three workgroups per CU measured ~2.5 % faster than 64-key tiles with
-    // two, and ~10 % slower under a causal mask (twice the masked diagonal
+    // three workgroups per CU measured ~4 % faster than 64-key tiles with
+    // two, and ~20 % slower under a causal mask (twice the masked diagonal
     // tiles and barriers), which keeps 64-key tiles
     {FA2_DTYPE_F32, 64, 0, FWD_PAIR(fa2_fwd_f32_kernel, 64, 32, 4, kMaskNone), 256, 128, 32, 3},
     {FA2_DTYPE_F32, 64, 1, FWD_PAIR(fa2_fwd_f32_kernel, 64, 64, 4, kMaskCausal), 256, 128, 64, 2},
