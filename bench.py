@@ -15,7 +15,7 @@ non-causal).  Prints ONE JSON line with the whole-job throughput
   against MI355X's dense MFMA peak for the dtype; traffic = HBM bytes per
   launch from the committed rocprofv3 counter summary, when it was taken on
   the current kernel source;
-* sclk: the shader clock the driver reports while the timed steps run;
+* sclk: the shader clock the amdgpu kernel driver reports (sysfs) while the timed steps run;
 * cpu_baseline: the CPU oracle timed on this host on the same workload
   (value), and on each of the five configurations with the max-abs error of
   the GPU's O and L against it (configs; the long-context one on its sample
