@@ -94,6 +94,9 @@ def test_split_kv_decode_shapes_auto(M, dtype):
     (33, 129, 4, 4, 3),      # explicit splits over a short key range
     (64, 1000, 2, 2, 0),     # the largest row count of the few-row kernels
     (65, 1000, 2, 2, 0),     # one row more: the 256-row kernels
+    (16, 4500, 8, 2, 3),     # splits of 1500 keys (D = 128, 16-bit, no mask: the four-buffer ring),
+                             # 47 tiles of 32 keys per split, the last one ragged
+    (4, 9000, 4, 4, 2),      # splits of 4500 keys: 141 tiles per split, one past a multiple of four
 ])
 def test_few_query_rows(M, N, H, Hk, n_splits, causal, D, dtype):
     # rows per (K/V) head <= 64 run the 64-row workgroups; the result must not
